@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the TN half-precision GEMM on one MI355X.
+
+One step = one ``mi_hgemm_run`` over the workload's synthetic operands (already
+resident in HBM), through the library's normal dispatch.  By default the
+operands rotate over enough copies that every call reads A and B from HBM
+rather than from the 256 MiB MALL ("cold"); ``--warm`` reuses one set.
+
+Prints ONE JSON line: throughput (TFLOP/s over the timed steps), the roofline
+of the dominant kernel (its per-launch duration from HIP events recorded on the
+launch stream inside the timed region), and the CPU oracle timed on a bounded
+sample of the same product on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload square|tiny|small|llm_MxNxK]
+                    [--mnk M_N_K] [--warm] [--no-cpu-baseline] [--all-configs OUT.jsonl]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HGEMM TFLOPS and µs/call per (M,N,K) on 1 MI355X; % of roofline"
+PEAK_MFMA_TFLOPS = 2516.6    # dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0        # HBM3E
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="square")
+    ap.add_argument("--mnk", default=None, help="custom shape M_N_K (randn/sqrt(K) inputs)")
+    ap.add_argument("--warm", action="store_true", help="reuse one operand set (MALL-resident)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--all-configs", default=None,
+                    help="also time every named workload and write JSON lines here")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (to scale "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path, encoding="utf-8") as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def problem_for(name, mnk):
+    from dense_fp16_gemm_hgemm_amd import inputs
+    if mnk:
+        M, N, K = (int(x) for x in mnk.split("_"))
+        s = 1.0 / math.sqrt(K)
+        return inputs.Problem(f"mnk_{M}x{N}x{K}", M, N, K, "randn", s, s, 7)
+    if name == "square":
+        return inputs.square()
+    if name == "tiny":
+        return inputs.tiny()
+    if name == "small":
+        return inputs.small(False)
+    for p in inputs.llm():
+        if p.name == name or p.name == "llm_" + name.replace("llm_", ""):
+            return p
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+class Workload:
+    """Device operand sets for one problem (copies of one seeded draw)."""
+
+    def __init__(self, p, cold: bool):
+        import torch
+        from dense_fp16_gemm_hgemm_amd import inputs
+        self.p = p
+        A, Bt = inputs.make(p)
+        self.A_host, self.Bt_host = A, Bt
+        dev = torch.device("cuda", 0)
+        a = torch.from_numpy(A).to(dev)
+        b = torch.from_numpy(Bt).to(dev)
+        set_bytes = p.min_bytes
+        nsets = 1
+        if cold:
+            nsets = max(2, math.ceil(2.2 * MALL_BYTES / max(set_bytes, 1)))
+            nsets = min(nsets, 2048)
+        self.sets = []
+        for s in range(nsets):
+            aa = a if s == 0 else a.clone()
+            bb = b if s == 0 else b.clone()
+            cc = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
+            self.sets.append((aa, bb, cc))
+        torch.cuda.synchronize()
+
+
+def time_steps(lib, wl, steps, warmup):
+    """Warm up, then time exactly `steps` launches bracketed by synchronisations.
+    Returns (ms per step, mean per-launch ms from event pairs, wall s)."""
+    import torch
+    sets = wl.sets
+    n = len(sets)
+    for i in range(warmup):
+        a, b, c = sets[i % n]
+        lib.run(a, b, c)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        a, b, c = sets[i % n]
+        ev[i][0].record(stream)
+        lib.run(a, b, c)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return total_ms / steps, statistics.fmean(per), wall, per
+
+
+def roofline(p, launch_ms, kernel, workload):
+    flops, nbytes = p.flops, p.min_bytes
+    t = launch_ms * 1e-3
+    ai = flops / nbytes
+    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        achieved, peak, unit, bound = flops / t / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = nbytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel, workload),
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
+
+
+def cpu_baseline(p, A, Bt, gpu_c, target_s):
+    """The oracle, as it is, on rows 0..R-1 of the product; R sized to ~target_s."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.default()
+
+    def rows(R):
+        r = np.repeat(np.arange(R, dtype=np.int64), p.N)
+        c = np.tile(np.arange(p.N, dtype=np.int64), R)
+        t0 = time.perf_counter()
+        vals = orc.hgemm_tn_entries(A, Bt, r, c)
+        return time.perf_counter() - t0, vals.reshape(R, p.N)
+
+    R0 = max(1, min(p.M, int(4e8 / (2 * p.N * p.K))))
+    t0, _ = rows(R0)
+    R = max(1, min(p.M, int(R0 * max(0.0, target_s - t0) / max(t0, 1e-6))))
+    t, vals = rows(R)
+    flop = 2.0 * R * p.N * p.K
+    # the sample doubles as a parity check of the timed GPU output
+    g = gpu_c[:R].astype(np.float64)
+    r64 = vals.astype(np.float64)
+    fin = np.isfinite(r64)
+    bound = 1e-3 * np.abs(r64[fin]).max() + 2e-3 * np.abs(r64[fin])
+    ok = bool(np.all(np.abs(g[fin] - r64[fin]) <= bound))
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"rows 0..{R - 1} of C ({R}x{p.N} outputs, K={p.K}) of {p.name}",
+            "sample_parity": "ok" if ok else "FAIL"}
+
+
+def torch_matmul_context(wl, steps=20):
+    """torch.matmul (the vendor BLAS) on the same operands, as context only."""
+    import torch
+    a, b, c = wl.sets[0]
+    for _ in range(3):
+        torch.matmul(a, b.t(), out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        a, b, c = wl.sets[i % len(wl.sets)]
+        torch.matmul(a, b.t(), out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return round(wl.p.flops / (ms * 1e-3) / 1e12, 2), round(ms * 1e3, 2)
+
+
+def measure(lib, p, steps, warmup, cold, with_torch=False):
+    wl = Workload(p, cold)
+    a, b, c = wl.sets[0]
+    kernel, gm, xcd = lib.plan(a, b, c)
+    ms, launch_ms, wall, per = time_steps(lib, wl, steps, warmup)
+    rec = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "kernel": kernel, "group_m": gm,
+           "xcd_remap": xcd, "cache": "cold" if cold else "warm", "sets": len(wl.sets),
+           "ms_per_step": ms, "us_per_call": round(launch_ms * 1e3, 3),
+           "us_per_call_median": round(statistics.median(per) * 1e3, 3),
+           "tflops": round(p.flops / (ms * 1e-3) / 1e12, 3), "wall_s": wall,
+           "roofline": roofline(p, launch_ms, kernel, p.name)}
+    if with_torch:
+        rec["torch_matmul_tflops"], rec["torch_matmul_us"] = torch_matmul_context(wl)
+    return rec, wl
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return
+    import dense_fp16_gemm_hgemm_amd as mh
+    lib = mh.Hgemm()
+    cold = not args.warm
+
+    if args.all_configs:
+        from dense_fp16_gemm_hgemm_amd import inputs
+        with open(args.all_configs, "w") as f:
+            for p in inputs.all_named():
+                if p.kind != "randn":
+                    continue
+                for c in (True, False):
+                    rec, _ = measure(lib, p, max(20, args.steps // 2), 5, c, with_torch=True)
+                    f.write(json.dumps(rec) + "\n")
+                    f.flush()
+                    print(f"# {p.name} {rec['cache']}: {rec['us_per_call']} us "
+                          f"{rec['tflops']} TFLOP/s ({rec['kernel']}) torch {rec['torch_matmul_us']} us",
+                          file=sys.stderr, flush=True)
+                torch.cuda.empty_cache()
+
+    p = problem_for(args.workload, args.mnk)
+    rec, wl = measure(lib, p, args.steps, args.warmup, cold, with_torch=True)
+    out = {
+        "metric": METRIC,
+        "value": rec["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(rec["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "layout": "TN",
+                   "accumulate": "fp32", "inputs": f"{p.kind} a*{p.a_scale:.6g} b*{p.b_scale:.6g} seed {p.seed}",
+                   "cache": rec["cache"], "operand_sets": rec["sets"], "kernel": rec["kernel"],
+                   "group_m": rec["group_m"], "xcd_remap": rec["xcd_remap"],
+                   "us_per_call": rec["us_per_call"], "us_per_call_median": rec["us_per_call_median"],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": rec["roofline"],
+        "cpu_baseline": None,
+        "context": {"torch_matmul_tflops": rec["torch_matmul_tflops"],
+                    "torch_matmul_us": rec["torch_matmul_us"],
+                    "source_digest": source_digest()},
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        gpu_c = wl.sets[(args.steps - 1) % len(wl.sets)][2].cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(p, wl.A_host, wl.Bt_host, gpu_c, args.cpu_seconds)
+    lib.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+// Compiled kernel instances of the TN half-precision GEMM and their registry.
+//
+// The instance set spans the tuner's search space (a9): workgroup tiles from
+// 16 to 256 in M and N, 4 or 8 waves, both gfx950 fp16 MFMA shapes, and the
+// skinny direct-to-register family for small M.  Tile sizes start from the
+// menus of "H100 GEMM L2驻留优化：warp-specialized TMA异步拷贝与RL调优策略"
+// (blog.hotdry.top), 可落地参数清单 (M 64/128, N 64/128 and the 32..512 log-spaced
+// search range) and "RL驱动CUDA L2 GEMM内核自动调优：A100/H100 tile size与融合优化"
+// (blog.hotdry.top), 正文 paragraph 3 and 落地参数与监控要点 (128x64 and 128x128
+// blocks, 4 warps), extended to 256 where the 160 KiB LDS of a gfx950 CU allows.
+#include "kernels.hpp"
+
+namespace mihg {
+
+// X-macro lists of the compiled instances.  Each list is expanded twice: into
+// explicit instantiations of the kernel templates (both compilation passes, so
+// the device code object holds every kernel) and into the registry (host pass).
+//   TILE:   X(BM, BN, WGM, WGN, MF)
+//   SKINNY: X(FM, FN, WAVES, UNROLL)
+#define MIHG_TILE_INSTANCES(X) \
+  X(256, 256, 2, 2, 32)          \
+  X(256, 256, 2, 4, 32)          \
+  X(256, 128, 2, 2, 32)          \
+  X(128, 256, 2, 2, 32)          \
+  X(256, 128, 4, 2, 32)          \
+  X(128, 128, 2, 2, 32)          \
+  X(128, 64, 2, 2, 32)           \
+  X(64, 128, 2, 2, 32)           \
+  X(64, 64, 2, 2, 32)            \
+  X(64, 64, 2, 2, 16)            \
+  X(32, 64, 1, 4, 16)            \
+  X(64, 32, 4, 1, 16)            \
+  X(32, 32, 2, 2, 16)            \
+  X(16, 64, 1, 2, 16)
+
+#define MIHG_SKINNY_INSTANCES(X) \
+  X(1, 1, 4, 4)                  \
+  X(1, 1, 8, 4)                  \
+  X(1, 2, 4, 4)                  \
+  X(1, 2, 8, 4)                  \
+  X(1, 4, 4, 2)                  \
+  X(2, 1, 8, 4)                  \
+  X(2, 2, 4, 4)                  \
+  X(4, 1, 4, 4)                  \
+  X(4, 1, 8, 2)                  \
+  X(4, 2, 4, 2)
+
+#define INSTANTIATE_TILE(BM, BN, WGM, WGN, MF) \
+  template __global__ void tile_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
+#define INSTANTIATE_SKINNY(FM, FN, W, U) \
+  template __global__ void skinny_kernel<FM, FN, W, U>(GemmArgs);
+template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
+MIHG_TILE_INSTANCES(INSTANTIATE_TILE)
+MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
+
+// The registry holds host launch functions, so it exists only in the host pass.
+#if !defined(__HIP_DEVICE_COMPILE__)
+#define TILE_DESC(BM, BN, WGM, WGN, MF)                                                     \
+  {"tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, 1, 1, \
+   2 * (BM + BN) * kLdsRow * 2, &launch_tile<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
+#define SKINNY_DESC(FM, FN, W, U)                                                          \
+  {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
+   W * 16 * FM * 16 * FN * 4, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
+
+const KernelDesc kKernels[] = {
+    // element-wise instance: any alignment, any leading dimensions (must stay first)
+    {"generic_64x64_w2x2_m32", FAMILY_TILE, 64, 64, 64, 4, 32, 0, 1, 128 * 64 * 2,
+     &launch_generic<64, 64, 2, 2, 32>, &grid_tile<64, 64>},
+    MIHG_TILE_INSTANCES(TILE_DESC)
+    MIHG_SKINNY_INSTANCES(SKINNY_DESC)
+};
+
+const int kNumKernels = (int)(sizeof(kKernels) / sizeof(kKernels[0]));
+#endif
+
+// ---------------------------------------------------------------------------
+__global__ void zero_fill_kernel(_Float16* C, int64_t ldc, int32_t M, int32_t N) {
+  const int64_t total = (int64_t)M * N;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / N, j = t - i * N;
+    C[i * ldc + j] = (_Float16)0.0f;
+  }
+}
+
+hipError_t launch_zero_fill(void* C, int64_t ldc, int32_t M, int32_t N, hipStream_t s) {
+  const int64_t total = (int64_t)M * N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<_Float16*>(C), ldc, M, N);
+  return hipGetLastError();
+}
+
+__device__ inline uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ void fill_small_int_kernel(_Float16* X, int64_t n, uint32_t seed) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t h = mix32((uint32_t)t ^ mix32(seed ^ (uint32_t)(t >> 32)));
+    X[t] = (_Float16)(float)((int)(h % 9u) - 4);
+  }
+}
+
+hipError_t launch_fill_small_int(void* X, int64_t n, uint32_t seed, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_small_int_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<_Float16*>(X), n, seed);
+  return hipGetLastError();
+}
+
+__global__ void count_mismatch_kernel(const uint16_t* X, const uint16_t* Y, int32_t M, int32_t N,
+                                      int64_t ld, int* count) {
+  const int64_t total = (int64_t)M * N;
+  int bad = 0;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / N, j = t - i * N;
+    const uint16_t x = X[i * ld + j], y = Y[i * ld + j];
+    bad += (x != y) && (((x | y) & 0x7fff) != 0);
+  }
+  if (bad) atomicAdd(count, bad);
+}
+
+hipError_t launch_count_mismatch(const void* X, const void* Y, int32_t M, int32_t N, int64_t ld,
+                                 int* d_count, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(d_count, 0, sizeof(int), s);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)M * N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(count_mismatch_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Y), M, N, ld,
+                     d_count);
+  return hipGetLastError();
+}
+
+}  // namespace mihg

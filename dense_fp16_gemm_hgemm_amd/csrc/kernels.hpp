@@ -1,0 +1,594 @@
+// HIP kernel templates of the TN half-precision GEMM for gfx950 (CDNA4).
+//
+// Pages this design follows (cited below by tag and section):
+//   [P1] "H100 GEMM L2驻留优化：warp-specialized TMA异步拷贝与RL调优策略"
+//        (blog.hotdry.top, 2025-12-05)
+//   [P2] "RL驱动CUDA L2 GEMM内核自动调优：A100/H100 tile size与融合优化"
+//        (blog.hotdry.top, 2025-12-05)
+//   [P3] "B-08. Hopper TMA：从单线程 Bulk Copy 到吞吐墙" (lqnn.cn)
+//
+// What is computed: C[i][j] = fp16_rne(sum_k A[i][k] * B[j][k]) with the sum in
+// fp32 on the matrix cores, A row-major, B column-major (stored as N rows of K
+// halves, i.e. both operands K-contiguous), C row-major ([P2] 正文 paragraphs 1
+// and 3).  The pages' dataflow (global -> shared -> registers -> tensor core ->
+// global, [P2] 正文 paragraph 3) maps onto gfx950 as
+//   global 16-byte loads -> XOR-swizzled LDS tile -> ds_read_b128 fragments ->
+//   v_mfma_f32_{32x32x16,16x16x32}_f16 -> fp16 convert -> global store,
+// with the next K tile's global loads in flight while the current tile's MFMAs
+// run (the prefetch that [P3] §2 and §5 show is where the overlap gain comes
+// from, and the multi-stage pipeline of [P1] 可落地参数清单 / [P2] 落地参数).
+//
+// MFMA operand layout used throughout (one wave of 64 lanes, instruction
+// MF x MF x KI with MF in {32, 16} and KI = 512 / MF):
+//   * lane l supplies row (l % MF) of the first source and column (l % MF) of
+//     the second source, 8 consecutive reduction elements each, starting at
+//     8 * (l / MF) within the instruction's KI;
+//   * the result element (r, c) of the MF x MF block sits in lane
+//     c + MF * ((r / 4) % (64 / MF)), register 4 * (r / (256 / MF)) + r % 4.
+// Both sources are loaded with the same k placement, so the sum is the same
+// dot product whatever order the hardware reduces in.  The first source is
+// the B tile (rows = output columns j), the second the A tile (columns =
+// output rows i), so each lane ends up owning 4 consecutive columns of one
+// output row, which makes the C stores 8-byte vectors along N.
+#pragma once
+
+#include "internal.h"
+
+namespace mihg {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int MF>
+struct Mfma;
+
+template <>
+struct Mfma<32> {
+  static constexpr int KI = 16;    // reduction depth per instruction
+  static constexpr int NACC = 16;  // fp32 results per lane
+  typedef f32x16 acc_t;
+  __device__ static inline acc_t mma(h8 a, h8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<16> {
+  static constexpr int KI = 32;
+  static constexpr int NACC = 4;
+  typedef f32x4 acc_t;
+  __device__ static inline acc_t mma(h8 a, h8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline h8 zero_h8() {
+  h8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (_Float16)0.0f;
+  return z;
+}
+
+// Workgroup id -> output tile (a2).  [P1] 正文 paragraph 2 and [P2] 正文
+// paragraph 3 put the lever in keeping operand panels cache-resident; on
+// MI355X each of the 8 XCDs has its own L2 and consecutive workgroup ids are
+// dispatched round-robin over the XCDs.  With xcd_remap the id is first
+// renumbered so that each XCD receives a contiguous range of logical ids; the
+// logical id is then walked in groups of group_m tile rows, so the workgroups
+// resident at one time share A row panels and B column panels.
+__device__ inline void tile_coords(int pid, int tiles_m, int tiles_n, int group_m,
+                                   int xcd_remap, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  if (xcd_remap) {
+    const int q = total >> 3, r = total & 7;
+    const int x = pid & 7, loc = pid >> 3;
+    pid = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + loc;
+  }
+  const int width = group_m * tiles_n;
+  const int group = pid / width;
+  const int first_m = group * group_m;
+  const int rows = min(tiles_m - first_m, group_m);
+  const int in = pid - group * width;
+  tm = first_m + in % rows;
+  tn = in / rows;
+}
+
+// LDS tile rows hold 64 halves = 8 chunks of 16 bytes.  The chunk index is
+// XORed with a function of the row (a3/a5): 16 consecutive rows read at one
+// logical chunk then touch 16 distinct (row parity, chunk) pairs and 8
+// consecutive rows 8 distinct chunks, so ds_read_b128 of an MFMA fragment and
+// ds_write_b128 of a loaded row are free of bank conflicts whether the LDS
+// serves 8 or 16 lanes of a b128 access per cycle.  [P3] §6.2 makes the point
+// that the swizzle has to be designed against the read pattern; [P1]
+// 可落地参数清单 uses the same 3-bit XOR (row bits into the 16-byte chunk index
+// of a 128-byte row).
+__device__ inline int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
+
+// Buffer resources (a8).  A raw buffer descriptor bounds every access by its
+// record count: loads past the end return 0 and stores past the end are
+// dropped.  Each workgroup builds descriptors whose range ends at the last
+// valid row of its tile, so rows beyond M or N need no code at all, and a
+// chunk beyond K is given the offset kOOB, which is outside every range.  This
+// is the zero-filled out-of-bounds behaviour [P3] §3.2 relies on for tile
+// copies, and it keeps the K loop free of branches.  Offsets are 32-bit; the
+// host only sends operands here whose tile rows span less than 2^31 bytes.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data format
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ inline h8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, h4 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+__device__ inline void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t off, _Float16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Tile family: BM x BN x 64 workgroup tiles, WGM x WGN waves, 2 LDS stages,
+// operands in the 16-byte alignment class.
+//
+// LDS rows are padded from 128 to 144 bytes (a3/a5).  A 16-byte read of row r
+// then starts at 4-byte bank 36*r mod 64: 16 consecutive rows read at one
+// chunk start at 16 distinct multiples of 4, and 8 consecutive rows at 8
+// distinct multiples of 4 mod 32, so the MFMA fragment reads (16 or 32 rows at
+// one chunk) are free of bank conflicts whether the LDS serves 8 or 16 lanes
+// of a ds_read_b128 per cycle.  [P3] §6.2 makes the point that the layout has
+// to be designed against the read pattern; padding instead of an XOR keeps
+// every fragment address a compile-time offset from one base register.
+//
+// Per K tile (one trip of the loop, a single basic block):
+//   * 16-byte buffer loads of tile k+1 into registers are issued first, so
+//     they are in flight during tile k's MFMAs (a4).  The row of each load
+//     slot and the K position are scalar offsets, so the loads cost no VALU;
+//   * tile k's fragments are read from LDS one MFMA step ahead of use
+//     (register double buffer), and the MFMAs run (a5, a6);
+//   * tile k+1 is written to the other LDS stage (a3) and one barrier ends the
+//     trip; the next tile's first fragments are read right after it, while
+//     the last MFMAs are still in the pipe.
+// The last trip loads a tile past K, which the descriptors turn into zeros.
+// When K is not a multiple of 64 the same loop runs with per-chunk K masks.
+constexpr int kLdsRow = 64 + 8;  // halves per padded LDS row
+
+// Instruction order of one K trip, handed to the machine scheduler as groups
+// (mask bits: 0x008 MFMA, 0x020 global read, 0x100 LDS read, 0x200 LDS write).
+// Left alone the scheduler sinks the next tile's global loads down to the LDS
+// writes that consume them and reads each fragment just before its MFMA; with
+// one or two waves per SIMD both expose a full memory latency to the matrix
+// pipe.  The order imposed here is, per MFMA step s:
+//   LDS reads of step s+1's fragments, then step s's MFMAs;
+// with the next tile's global loads spread over the first step's MFMAs and its
+// LDS writes over the last step's, so every latency sits behind MFMA work.
+template <int NM, int NR, int NG, int KSTEPS>
+__device__ __forceinline__ void trip_schedule() {
+  constexpr int PER = (NG + NM - 1) / NM;  // loads (or LDS writes) per MFMA
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    if (s + 1 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (s == 0 && i * PER < NG) __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);
+      if (s == KSTEPS - 1 && i * PER < NG) __builtin_amdgcn_sched_group_barrier(0x200, PER, 0);
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF, bool MASK_K>
+__device__ __forceinline__ void tile_main_loop(
+    const GemmArgs& p, _Float16 (*lds)[(BM + BN) * kLdsRow], __amdgpu_buffer_rsrc_t rsa,
+    __amdgpu_buffer_rsrc_t rsb, typename Mfma<MF>::acc_t (&acc)[BM / WGM / MF][BN / WGN / MF]) {
+  using MM = Mfma<MF>;
+  constexpr int BK = 64, CPR = BK / 8;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int KSTEPS = BK / MM::KI;
+  constexpr int A_IT = BM * CPR / NT, B_IT = BN * CPR / NT;
+  constexpr int ROWS_PER_IT = NT / CPR;
+  static_assert(KSTEPS % 2 == 0, "fragment double buffer needs an even step count");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int K = p.K;
+  const int c = tid % CPR, r0 = tid / CPR;
+  // global: lane part of the offset in a VGPR, slot row and K position scalar
+  const uint32_t a_voff = (uint32_t)(r0 * p.lda * 2 + c * 16);
+  const uint32_t b_voff = (uint32_t)(r0 * p.ldb * 2 + c * 16);
+  const uint32_t a_row_step = (uint32_t)(ROWS_PER_IT * p.lda * 2);
+  const uint32_t b_row_step = (uint32_t)(ROWS_PER_IT * p.ldb * 2);
+  // LDS: write slot and fragment bases (halves); everything else is immediate
+  const int w_base = r0 * kLdsRow + c * 8;
+  const int fa_base = (wm * WTM + lane % MF) * kLdsRow + (lane / MF) * 8;
+  const int fb_base = BM * kLdsRow + (wn * WTN + lane % MF) * kLdsRow + (lane / MF) * 8;
+
+  h8 ra[A_IT], rb[B_IT];
+  auto gload = [&](int k0) {
+    const uint32_t kb = (uint32_t)k0 * 2;
+    bool kin = true;
+    if constexpr (MASK_K) kin = k0 + c * 8 < K;
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+      const uint32_t voff = MASK_K ? (kin ? a_voff : kOOB) : a_voff;
+      ra[it] = __builtin_bit_cast(
+          h8, __builtin_amdgcn_raw_buffer_load_b128(rsa, voff, it * a_row_step + kb, 0));
+    }
+#pragma unroll
+    for (int it = 0; it < B_IT; ++it) {
+      const uint32_t voff = MASK_K ? (kin ? b_voff : kOOB) : b_voff;
+      rb[it] = __builtin_bit_cast(
+          h8, __builtin_amdgcn_raw_buffer_load_b128(rsb, voff, it * b_row_step + kb, 0));
+    }
+  };
+  auto sstore = [&](int s) {
+    _Float16* st = lds[s] + w_base;
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it)
+      *reinterpret_cast<h8*>(st + it * ROWS_PER_IT * kLdsRow) = ra[it];
+#pragma unroll
+    for (int it = 0; it < B_IT; ++it)
+      *reinterpret_cast<h8*>(st + (BM + it * ROWS_PER_IT) * kLdsRow) = rb[it];
+  };
+  h8 fa[2][FM], fb[2][FN];
+  auto fread = [&](int s, int step, int buf) {
+    const _Float16* st = lds[s];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      fa[buf][fm] = *reinterpret_cast<const h8*>(st + fa_base + fm * MF * kLdsRow + step * MM::KI);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      fb[buf][fn] = *reinterpret_cast<const h8*>(st + fb_base + fn * MF * kLdsRow + step * MM::KI);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  fread(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    gload((kt + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      if (s + 1 < KSTEPS) fread(cur, s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = MM::mma(fb[s & 1][fn], fa[s & 1][fm], acc[fm][fn]);
+    }
+    sstore(cur ^ 1);
+    trip_schedule<FM * FN, FM + FN, A_IT + B_IT, KSTEPS>();
+    __syncthreads();
+    fread(cur ^ 1, 0, 0);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+tile_kernel(GemmArgs p) {
+  using MM = Mfma<MF>;
+  constexpr int CPR = 8;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile chunks must split evenly");
+
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][(BM + BN) * kLdsRow];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+  const auto rsa = make_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const auto rsb = make_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  if ((K & 63) == 0)
+    tile_main_loop<BM, BN, WGM, WGN, MF, false>(p, lds, rsa, rsb, acc);
+  else
+    tile_main_loop<BM, BN, WGM, WGN, MF, true>(p, lds, rsa, rsb, acc);
+
+  // Epilogue (a7): fp32 -> fp16 round-to-nearest-even, alpha = 1, beta = 0;
+  // 8-byte stores along N, rows beyond M dropped by the descriptor.
+  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          h4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][4 * g + e];
+          buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                       (_Float16)acc[fm][fn][4 * g + e]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Element-wise instance: any alignment, any leading dimensions (a8).  Same
+// tiling and arithmetic as the tile family, but every global access is a
+// 2-byte access with its own bounds check; it exists for operands outside the
+// 16-byte class and as the tuner's reference.
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+generic_kernel(GemmArgs p) {
+  using MM = Mfma<MF>;
+  constexpr int BK = 64, CPR = BK / 8;
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int KSTEPS = BK / MM::KI;
+  constexpr int A_IT = BM * CPR / NT, B_IT = BN * CPR / NT;
+  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile chunks must split evenly");
+
+  __shared__ __attribute__((aligned(16))) _Float16 lds[(BM + BN) * BK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const _Float16* __restrict__ A = static_cast<const _Float16*>(p.A);
+  const _Float16* __restrict__ B = static_cast<const _Float16*>(p.B);
+  _Float16* __restrict__ C = static_cast<_Float16*>(p.C);
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+      const int idx = tid + it * NT, row = idx / CPR, c = idx % CPR;
+      const int gm = m0 + row, gk = k0 + c * 8;
+      h8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (gm < M && gk + e < K) ? A[gm * lda + gk + e] : (_Float16)0.0f;
+      *reinterpret_cast<h8*>(lds + row * BK + swz(row, c) * 8) = v;
+    }
+#pragma unroll
+    for (int it = 0; it < B_IT; ++it) {
+      const int idx = tid + it * NT, row = idx / CPR, c = idx % CPR;
+      const int gn = n0 + row, gk = k0 + c * 8;
+      h8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (gn < N && gk + e < K) ? B[gn * ldb + gk + e] : (_Float16)0.0f;
+      *reinterpret_cast<h8*>(lds + BM * BK + row * BK + swz(row, c) * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int c = ks * (MM::KI / 8) + lane / MF;
+      h8 af[FM], bf[FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm * WTM + fm * MF + lane % MF;
+        af[fm] = *reinterpret_cast<const h8*>(lds + row * BK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int row = wn * WTN + fn * MF + lane % MF;
+        bf[fn] = *reinterpret_cast<const h8*>(lds + BM * BK + row * BK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(bf[fn], af[fm], acc[fm][fn]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int i = m0 + wm * WTM + fm * MF + lane % MF;
+    if (i >= M) continue;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int g = 0; g < MM::NACC / 4; ++g) {
+        const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < N) C[i * ldc + j + e] = (_Float16)acc[fm][fn][4 * g + e];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny family (small M): no LDS staging of operands.  Each workgroup owns a
+// (16*FM) x (16*FN) output tile; its WAVES waves split the K range into
+// contiguous slices and stream A and B fragments straight from global memory
+// into registers in the 16x16x32 MFMA layout, UNROLL k-steps per load group,
+// with the next group's loads issued before the current group's MFMAs.  The
+// per-wave fp32 partial tiles are summed through LDS in wave order (so the
+// result does not depend on timing) and converted once.  B, the large operand
+// for these shapes, is read exactly once; A is re-read from L2.
+// Requires the 16-byte alignment class.
+template <int FM, int FN, int WAVES, int UNROLL>
+__global__ void __launch_bounds__(64 * WAVES)
+skinny_kernel(GemmArgs p) {
+  using MM = Mfma<16>;
+  constexpr int BM = 16 * FM, BN = 16 * FN;
+  __shared__ __attribute__((aligned(16))) float red[WAVES][BM * BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const _Float16* A = static_cast<const _Float16*>(p.A);
+  const _Float16* B = static_cast<const _Float16*>(p.B);
+  _Float16* C = static_cast<_Float16*>(p.C);
+
+  const int r = lane & 15, q = lane >> 4;
+  // rows beyond M / N fall outside the descriptors' ranges and read as 0
+  const auto rsa = make_rsrc(A + m0 * p.lda, (uint32_t)(min(BM, M - m0) * p.lda * 2));
+  const auto rsb = make_rsrc(B + n0 * p.ldb, (uint32_t)(min(BN, N - n0) * p.ldb * 2));
+  uint32_t a_off[FM], b_off[FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) a_off[fm] = (uint32_t)((fm * 16 + r) * p.lda * 2 + q * 16);
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) b_off[fn] = (uint32_t)((fn * 16 + r) * p.ldb * 2 + q * 16);
+
+  const int steps = (K + MM::KI - 1) / MM::KI;
+  const int s_begin = (int)((int64_t)steps * wave / WAVES);
+  const int s_end = (int)((int64_t)steps * (wave + 1) / WAVES);
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[fm][fn][v] = 0.0f;
+
+  h8 af[2][UNROLL][FM], bf[2][UNROLL][FN];
+  auto load = [&](int buf, int s0) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int s = s0 + u;
+      const int k = s * MM::KI;
+      const bool kin = s < s_end && k + q * 8 < K;
+      const uint32_t kb = (uint32_t)k * 2;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) af[buf][u][fm] = buf_load16(rsa, kin ? a_off[fm] + kb : kOOB);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) bf[buf][u][fn] = buf_load16(rsb, kin ? b_off[fn] + kb : kOOB);
+    }
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = MM::mma(bf[buf][u][fn], af[buf][u][fm], acc[fm][fn]);
+  };
+
+  if (s_begin < s_end) {
+    load(0, s_begin);
+    int s = s_begin;
+    for (; s + UNROLL < s_end; s += 2 * UNROLL) {
+      load(1, s + UNROLL);
+      compute(0);
+      load(0, s + 2 * UNROLL);  // past s_end: every slot reads as 0
+      compute(1);
+    }
+    if (s < s_end) compute(0);
+  }
+
+  // partial tiles -> LDS, summed in wave order
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[wave][(fm * 16 + r) * BN + fn * 16 + 4 * q + v] = acc[fm][fn][v];
+  __syncthreads();
+  _Float16* Cw = C + m0 * p.ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * p.ldc * 2));
+  const bool n_quads = (N & 3) == 0;
+  for (int e = tid; e < BM * BN / 4; e += 64 * WAVES) {
+    const int ii = (e * 4) / BN, jj = (e * 4) % BN;
+    const int j = n0 + jj;
+    f32x4 s = *reinterpret_cast<const f32x4*>(&red[0][ii * BN + jj]);
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) s += *reinterpret_cast<const f32x4*>(&red[w][ii * BN + jj]);
+    h4 o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = (_Float16)s[t];
+    const uint32_t off = (uint32_t)((ii * p.ldc + j) * 2);
+    if (n_quads) {
+      buf_store8(rsc, j < N ? off : kOOB, o);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) buf_store2(rsc, j + t < N ? off + 2 * t : kOOB, o[t]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+template <int BM, int BN, int WGM, int WGN, int MF>
+hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((tile_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g), dim3(64 * WGM * WGN),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF>
+hipError_t launch_generic(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((generic_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+int64_t grid_tile(int32_t M, int32_t N) {
+  return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+}
+
+template <int FM, int FN, int WAVES, int UNROLL>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + 16 * FM - 1) / (16 * FM)) * ((a.N + 16 * FN - 1) / (16 * FN));
+  hipLaunchKernelGGL((skinny_kernel<FM, FN, WAVES, UNROLL>), dim3((unsigned)g), dim3(64 * WAVES),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mihg

@@ -1,0 +1,600 @@
+// Host side of libmi_hgemm: the C ABI declared in include/mi_hgemm.h.
+//
+// Pages this follows:
+//   [P1] "H100 GEMM L2驻留优化：warp-specialized TMA异步拷贝与RL调优策略" (blog.hotdry.top)
+//   [P2] "RL驱动CUDA L2 GEMM内核自动调优：A100/H100 tile size与融合优化" (blog.hotdry.top)
+//   [P3] "B-08. Hopper TMA：从单线程 Bulk Copy 到吞吐墙" (lqnn.cn)
+//
+// Responsibilities:
+//   * argument validation and status codes (the alignment rules of [P3] §3.1
+//     and §6.1: misaligned vector copies are undefined, so alignment is decided
+//     on the host and misaligned operands take the element-wise instance);
+//   * dispatch (a1): (M, N, K, alignment class) -> table entry, else the nearest
+//     tuned shape, else built-in heuristics -> one launch on the caller's
+//     stream, with nothing rebuilt or allocated per call ([P3] §8 lists
+//     per-launch rebuilding as a classic mistake);
+//   * the shape -> config table file and the tuner (a9), which replaces the
+//     pages' RL agent ([P1] 正文 paragraph 4, [P2] 正文 paragraph 2) with an
+//     exhaustive or pruned timed sweep over the compiled instances and raster
+//     settings, checked for correctness before it may win.
+#include <dlfcn.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/mi_hgemm.h"
+#include "internal.h"
+
+namespace {
+
+using mihg::GemmArgs;
+using mihg::KernelDesc;
+using mihg::kKernels;
+using mihg::kNumKernels;
+
+constexpr int kGenericKernel = 0;   // element-wise instance, any alignment
+constexpr const char* kArch = "gfx950";
+
+struct Config {
+  int32_t kernel = kGenericKernel;
+  int32_t group_m = 1;
+  int32_t xcd = 0;
+  double us = 0.0;  // measured time when tuned; 0 for heuristic picks
+};
+
+struct Key {
+  int64_t M, N, K;
+  int32_t aligned;
+  bool operator<(const Key& o) const {
+    return std::tie(M, N, K, aligned) < std::tie(o.M, o.N, o.K, o.aligned);
+  }
+};
+
+}  // namespace
+
+struct mi_hgemm_ctx {
+  int device = -1;
+  bool no_device = false;
+  int last_hip_error = 0;
+  std::string table_path;  // resolved path (may be empty)
+  std::map<Key, Config> table;
+  std::mutex mu;           // guards table updates (tune) and last_hip_error
+};
+
+namespace {
+
+bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int find_kernel(const char* name) {
+  for (int i = 0; i < kNumKernels; ++i)
+    if (std::strcmp(kKernels[i].name, name) == 0) return i;
+  return -1;
+}
+
+// Shared argument checks of run, plan and run_kernel.
+mi_hgemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                           const void* B, int64_t ldb, const void* C, int64_t ldc,
+                           mi_hgemm_layout_t layout) {
+  if (layout != MI_HGEMM_LAYOUT_TN) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return MI_HGEMM_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (lda < std::max<int64_t>(K, 1) || ldb < std::max<int64_t>(K, 1) ||
+      ldc < std::max<int64_t>(N, 1))
+    return MI_HGEMM_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return MI_HGEMM_OK;
+  if (C == nullptr) return MI_HGEMM_ERR_INVALID_ARG;
+  if (K > 0 && (A == nullptr || B == nullptr)) return MI_HGEMM_ERR_INVALID_ARG;
+  // C must not overlap the operands it is computed from.
+  const uintptr_t c0 = reinterpret_cast<uintptr_t>(C);
+  const uintptr_t c1 = c0 + 2u * (uintptr_t)((M - 1) * ldc + N);
+  auto overlaps = [&](const void* X, int64_t rows, int64_t ld, int64_t cols) {
+    if (rows == 0 || cols == 0) return false;
+    const uintptr_t x0 = reinterpret_cast<uintptr_t>(X);
+    const uintptr_t x1 = x0 + 2u * (uintptr_t)((rows - 1) * ld + cols);
+    return x0 < c1 && c0 < x1;
+  };
+  if (K > 0 && (overlaps(A, M, lda, K) || overlaps(B, N, ldb, K))) return MI_HGEMM_ERR_INVALID_ARG;
+  return MI_HGEMM_OK;
+}
+
+// The vector-load kernels address a tile through 32-bit buffer offsets, so
+// their leading dimensions are capped at kMaxVectorLd elements (a 256-row tile
+// then spans at most 2^30 bytes).
+constexpr int64_t kMaxVectorLd = int64_t(1) << 21;
+
+bool aligned_class(int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   const void* C, int64_t ldc) {
+  return (K % 8) == 0 && (lda % 8) == 0 && (ldb % 8) == 0 && (ldc % 8) == 0 &&
+         lda <= kMaxVectorLd && ldb <= kMaxVectorLd && ldc <= kMaxVectorLd &&
+         is_aligned16(A) && is_aligned16(B) && is_aligned16(C);
+}
+
+// Built-in choice when the table has nothing close.  Small M streams B through
+// the skinny family; otherwise the largest LDS tile that still gives every CU
+// a workgroup ([P2] 正文 paragraph 3: large tiles raise reuse and lower
+// occupancy, so the tile is the largest that keeps the machine full).
+Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
+  Config c;
+  if (!aligned) return c;
+  (void)K;
+  if (M <= 64) {
+    const char* name = M <= 16 ? "skinny_1x1_w8_u4" : M <= 32 ? "skinny_2x1_w8_u4" : "skinny_4x1_w8_u2";
+    c.kernel = find_kernel(name);
+    if (c.kernel < 0) c.kernel = kGenericKernel;
+    return c;
+  }
+  static const char* const order[] = {"tile_256x256_w2x2_m32", "tile_256x128_w2x2_m32",
+                                      "tile_128x128_w2x2_m32", "tile_128x64_w2x2_m32",
+                                      "tile_64x64_w2x2_m32"};
+  const int n = (int)(sizeof(order) / sizeof(order[0]));
+  for (int t = 0; t < n; ++t) {
+    const int k = find_kernel(order[t]);
+    if (k < 0) continue;
+    c.kernel = k;
+    if (kKernels[k].grid((int32_t)M, (int32_t)N) >= 256) break;
+  }
+  c.group_m = 8;
+  c.xcd = 1;
+  return c;
+}
+
+Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
+  const Key key{M, N, K, aligned ? 1 : 0};
+  auto it = h->table.find(key);
+  if (it != h->table.end()) return it->second;
+  // nearest tuned shape in log2(M, N, K), within a factor of two overall
+  double best = 1.0 + 1e-9;
+  const Config* pick = nullptr;
+  for (const auto& kv : h->table) {
+    if (kv.first.aligned != key.aligned) continue;
+    const double d = std::fabs(std::log2((double)M / kv.first.M)) +
+                     std::fabs(std::log2((double)N / kv.first.N)) +
+                     std::fabs(std::log2((double)K / kv.first.K));
+    if (d <= best) {
+      best = d;
+      pick = &kv.second;
+    }
+  }
+  if (pick) return *pick;
+  return heuristic(M, N, K, aligned);
+}
+
+// Table file: one entry per line,
+//   <arch> <M> <N> <K> <layout> <a16|any> <kernel name> <group_m> <xcd_remap> <microseconds>
+// '#' starts a comment.  Lines for another arch or layout are skipped; lines
+// that do not parse, or name an unknown kernel, mark the table as damaged.
+bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
+  *file_missing = false;
+  FILE* f = std::fopen(path.c_str(), "r");
+  if (!f) {
+    *file_missing = true;
+    return false;
+  }
+  bool clean = true;
+  char line[512];
+  while (std::fgets(line, sizeof line, f)) {
+    char* p = line;
+    while (*p == ' ' || *p == '\t') ++p;
+    if (*p == '#' || *p == '\n' || *p == '\r' || *p == '\0') continue;
+    char arch[64], layout[16], align[16], kname[128];
+    long long M, N, K;
+    int gm, xcd;
+    double us;
+    const int got = std::sscanf(p, "%63s %lld %lld %lld %15s %15s %127s %d %d %lf", arch, &M, &N,
+                                &K, layout, align, kname, &gm, &xcd, &us);
+    if (got != 10 || M < 1 || N < 1 || K < 1 || gm < 1 || (xcd != 0 && xcd != 1)) {
+      clean = false;
+      continue;
+    }
+    if (std::strcmp(arch, kArch) != 0 || std::strcmp(layout, "TN") != 0) continue;
+    const int k = find_kernel(kname);
+    const bool al = std::strcmp(align, "a16") == 0;
+    if (k < 0 || (!al && std::strcmp(align, "any") != 0) || (!al && kKernels[k].aligned)) {
+      clean = false;
+      continue;
+    }
+    Config c;
+    c.kernel = k;
+    c.group_m = gm;
+    c.xcd = xcd;
+    c.us = us;
+    h->table[Key{M, N, K, al ? 1 : 0}] = c;
+  }
+  std::fclose(f);
+  return clean;
+}
+
+bool write_entry(FILE* f, const Key& k, const Config& c) {
+  return std::fprintf(f, "%s %lld %lld %lld TN %s %s %d %d %.3f\n", kArch, (long long)k.M,
+                      (long long)k.N, (long long)k.K, k.aligned ? "a16" : "any",
+                      kKernels[c.kernel].name, c.group_m, c.xcd, c.us) > 0;
+}
+
+std::string default_table_path() {
+  Dl_info info;
+  if (dladdr(reinterpret_cast<void*>(&default_table_path), &info) && info.dli_fname) {
+    std::string so = info.dli_fname;
+    const size_t slash = so.rfind('/');
+    const std::string dir = slash == std::string::npos ? "." : so.substr(0, slash);
+    return dir + "/tables/gfx950.tsv";
+  }
+  return std::string();
+}
+
+mi_hgemm_status_t hip_fail(mi_hgemm_ctx* h, hipError_t e) {
+  if (h) {
+    std::lock_guard<std::mutex> lk(h->mu);
+    h->last_hip_error = (int)e;
+  }
+  return MI_HGEMM_ERR_HIP;
+}
+
+// Makes the handle's device current for the scope of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool switched = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      switched = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (switched) (void)hipSetDevice(prev);
+  }
+};
+
+mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, hipStream_t stream) {
+  const KernelDesc& kd = kKernels[c.kernel];
+  if (kd.grid((int32_t)M, (int32_t)N) > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+  GemmArgs a;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.group_m = std::max(1, c.group_m);
+  a.xcd_remap = c.xcd ? 1 : 0;
+  a.pad_ = 0;
+  const hipError_t e = kd.launch(a, stream);
+  if (e != hipSuccess) return hip_fail(h, e);
+  return MI_HGEMM_OK;
+}
+
+mi_hgemm_status_t run_config(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N, int64_t K,
+                             const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                             int64_t ldc, void* stream) {
+  if (M == 0 || N == 0) return MI_HGEMM_OK;
+  if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
+  DeviceGuard g(h->device);
+  if (g.err != hipSuccess) return hip_fail(h, g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) {
+    const hipError_t e = mihg::launch_zero_fill(C, ldc, (int32_t)M, (int32_t)N, s);
+    return e == hipSuccess ? MI_HGEMM_OK : hip_fail(h, e);
+  }
+  return launch(h, c, M, N, K, A, lda, B, ldb, C, ldc, s);
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- C ABI ---
+extern "C" {
+
+const char* mi_hgemm_status_string(mi_hgemm_status_t s) {
+  switch (s) {
+    case MI_HGEMM_OK: return "MI_HGEMM_OK";
+    case MI_HGEMM_ERR_INVALID_ARG: return "MI_HGEMM_ERR_INVALID_ARG";
+    case MI_HGEMM_ERR_UNSUPPORTED: return "MI_HGEMM_ERR_UNSUPPORTED";
+    case MI_HGEMM_ERR_NO_DEVICE: return "MI_HGEMM_ERR_NO_DEVICE";
+    case MI_HGEMM_ERR_HIP: return "MI_HGEMM_ERR_HIP";
+    case MI_HGEMM_ERR_IO: return "MI_HGEMM_ERR_IO";
+    case MI_HGEMM_WARN_TABLE_DEFAULTS: return "MI_HGEMM_WARN_TABLE_DEFAULTS";
+  }
+  return "MI_HGEMM_UNKNOWN_STATUS";
+}
+
+mi_hgemm_status_t mi_hgemm_create_ex(mi_hgemm_handle_t* out, const char* table_path,
+                                     uint32_t flags) {
+  if (!out) return MI_HGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  mi_hgemm_ctx* h = new (std::nothrow) mi_hgemm_ctx();
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  if (flags & MI_HGEMM_CREATE_NO_DEVICE) {
+    h->no_device = true;
+  } else {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count < 1 || hipGetDevice(&h->device) != hipSuccess) {
+      delete h;
+      return MI_HGEMM_ERR_NO_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, h->device) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, kArch, std::strlen(kArch)) != 0) {
+      delete h;
+      return MI_HGEMM_ERR_NO_DEVICE;
+    }
+  }
+  bool named = false;
+  if (table_path && *table_path) {
+    h->table_path = table_path;
+    named = true;
+  } else if (const char* env = std::getenv("MI_HGEMM_TABLE"); env && *env) {
+    h->table_path = env;
+    named = true;
+  } else {
+    h->table_path = default_table_path();
+  }
+  mi_hgemm_status_t st = MI_HGEMM_OK;
+  if (!h->table_path.empty()) {
+    bool missing = false;
+    const bool clean = load_table(h, h->table_path, &missing);
+    if ((missing && named) || (!missing && !clean)) st = MI_HGEMM_WARN_TABLE_DEFAULTS;
+  }
+  *out = h;
+  return st;
+}
+
+mi_hgemm_status_t mi_hgemm_create(mi_hgemm_handle_t* out, const char* table_path) {
+  return mi_hgemm_create_ex(out, table_path, 0u);
+}
+
+mi_hgemm_status_t mi_hgemm_destroy(mi_hgemm_handle_t h) {
+  delete h;
+  return MI_HGEMM_OK;
+}
+
+int mi_hgemm_last_hip_error(mi_hgemm_handle_t h) {
+  if (!h) return 0;
+  std::lock_guard<std::mutex> lk(h->mu);
+  return h->last_hip_error;
+}
+
+int mi_hgemm_kernel_count(void) { return kNumKernels; }
+
+const char* mi_hgemm_kernel_name(int index) {
+  return (index >= 0 && index < kNumKernels) ? kKernels[index].name : nullptr;
+}
+
+mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                const void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  Config c;
+  c.kernel = -1;
+  if (M > 0 && N > 0 && K > 0) c = select(h, M, N, K, aligned_class(K, A, lda, B, ldb, C, ldc));
+  if (kernel_index) *kernel_index = c.kernel;
+  if (group_m) *group_m = c.group_m;
+  if (xcd_remap) *xcd_remap = c.xcd;
+  return MI_HGEMM_OK;
+}
+
+mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                               int64_t ldc, mi_hgemm_layout_t layout, void* stream) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  if (M == 0 || N == 0) return MI_HGEMM_OK;
+  Config c;
+  if (K > 0) c = select(h, M, N, K, aligned_class(K, A, lda, B, ldb, C, ldc));
+  return run_config(h, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index, int32_t group_m,
+                                      int32_t xcd_remap, int64_t M, int64_t N, int64_t K,
+                                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                                      void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                      void* stream) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  if (kernel_index < 0 || kernel_index >= kNumKernels) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1)) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  if (kKernels[kernel_index].aligned && !aligned_class(K, A, lda, B, ldb, C, ldc))
+    return MI_HGEMM_ERR_UNSUPPORTED;
+  Config c;
+  c.kernel = kernel_index;
+  c.group_m = group_m;
+  c.xcd = xcd_remap;
+  return run_config(h, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int mi_hgemm_table_size(mi_hgemm_handle_t h) {
+  if (!h) return 0;
+  std::lock_guard<std::mutex> lk(h->mu);
+  return (int)h->table.size();
+}
+
+mi_hgemm_status_t mi_hgemm_table_save(mi_hgemm_handle_t h, const char* path) {
+  if (!h || !path) return MI_HGEMM_ERR_INVALID_ARG;
+  FILE* f = std::fopen(path, "w");
+  if (!f) return MI_HGEMM_ERR_IO;
+  bool ok = std::fprintf(f, "# arch M N K layout align kernel group_m xcd_remap us\n") > 0;
+  {
+    std::lock_guard<std::mutex> lk(h->mu);
+    for (const auto& kv : h->table) ok = ok && write_entry(f, kv.first, kv.second);
+  }
+  ok = (std::fclose(f) == 0) && ok;
+  return ok ? MI_HGEMM_OK : MI_HGEMM_ERR_IO;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ tuner --
+namespace {
+
+struct Scratch {
+  void* p = nullptr;
+  ~Scratch() {
+    if (p) (void)hipFree(p);
+  }
+};
+
+double median(std::vector<double> v) {
+  std::sort(v.begin(), v.end());
+  return v.empty() ? 0.0 : v[v.size() / 2];
+}
+
+}  // namespace
+
+extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                           mi_hgemm_layout_t layout, void* stream,
+                                           uint32_t flags) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  if (layout != MI_HGEMM_LAYOUT_TN) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (M < 1 || N < 1 || K < 1) return MI_HGEMM_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+  // Only the 16-byte class has a choice to make; K and N must allow it.
+  if (K % 8 != 0 || K > kMaxVectorLd || N > kMaxVectorLd) return MI_HGEMM_ERR_UNSUPPORTED;
+  // Integer scratch operands stay exact in fp32 only while 16*K < 2^24.
+  if (K >= (1 << 20)) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
+  DeviceGuard g(h->device);
+  if (g.err != hipSuccess) return hip_fail(h, g.err);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ldc = (N + 7) / 8 * 8;
+
+  Scratch a, b, c, cref, cnt;
+  hipError_t e;
+  if ((e = hipMalloc(&a.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&b.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&c.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&cref.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&cnt.p, sizeof(int))) != hipSuccess) return hip_fail(h, e);
+  if ((e = mihg::launch_fill_small_int(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
+  if ((e = mihg::launch_fill_small_int(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
+
+  // Reference result: the element-wise instance.
+  Config ref;
+  mi_hgemm_status_t st = launch(h, ref, M, N, K, a.p, K, b.p, K, cref.p, ldc, s);
+  if (st != MI_HGEMM_OK) return st;
+
+  hipEvent_t ev0, ev1;
+  if ((e = hipEventCreate(&ev0)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipEventCreate(&ev1)) != hipSuccess) {
+    (void)hipEventDestroy(ev0);
+    return hip_fail(h, e);
+  }
+
+  const bool heuristic_only = (flags & MI_HGEMM_TUNE_HEURISTIC) != 0;
+  const Config start = heuristic(M, N, K, true);
+  std::vector<Config> cands;
+  for (int k = 0; k < kNumKernels; ++k) {
+    const KernelDesc& kd = kKernels[k];
+    if (!kd.aligned) continue;
+    if (kd.grid((int32_t)M, (int32_t)N) > INT32_MAX) continue;
+    if (kd.family == mihg::FAMILY_TILE) {
+      static const int rasters[][2] = {{1, 0}, {4, 0}, {8, 0}, {16, 0}, {1, 1}, {4, 1}, {8, 1}, {16, 1}};
+      for (const auto& r : rasters) {
+        if (heuristic_only && !((r[0] == 8 && r[1] == 1) || (r[0] == 1 && r[1] == 0))) continue;
+        Config c;
+        c.kernel = k;
+        c.group_m = r[0];
+        c.xcd = r[1];
+        cands.push_back(c);
+      }
+    } else {
+      if (heuristic_only && M > 128) continue;
+      Config c;
+      c.kernel = k;
+      cands.push_back(c);
+    }
+  }
+  if (std::find_if(cands.begin(), cands.end(), [&](const Config& c) {
+        return c.kernel == start.kernel && c.group_m == start.group_m && c.xcd == start.xcd;
+      }) == cands.end())
+    cands.push_back(start);
+
+  Config best;
+  best.kernel = -1;
+  double best_us = 1e300;
+  mi_hgemm_status_t result = MI_HGEMM_OK;
+  for (const Config& cand : cands) {
+    // correctness first: bit-identical to the reference on exact integer data
+    st = launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
+    if (st != MI_HGEMM_OK) {
+      result = st;
+      break;
+    }
+    if ((e = mihg::launch_count_mismatch(c.p, cref.p, (int32_t)M, (int32_t)N, ldc,
+                                         static_cast<int*>(cnt.p), s)) != hipSuccess) {
+      result = hip_fail(h, e);
+      break;
+    }
+    int bad = -1;
+    if ((e = hipMemcpyAsync(&bad, cnt.p, sizeof(int), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+      result = hip_fail(h, e);
+      break;
+    }
+    if (bad != 0) continue;  // a wrong candidate never wins
+    // time: size the repeat count to ~1 ms per trial, median of 5 trials
+    float ms = 0.f;
+    (void)hipEventRecord(ev0, s);
+    (void)launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
+    (void)hipEventRecord(ev1, s);
+    if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
+      result = hip_fail(h, e);
+      break;
+    }
+    (void)hipEventElapsedTime(&ms, ev0, ev1);
+    int reps = (int)std::min(200.0, std::max(1.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
+    std::vector<double> trials;
+    for (int t = 0; t < 5; ++t) {
+      (void)hipEventRecord(ev0, s);
+      for (int r = 0; r < reps; ++r) (void)launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
+      (void)hipEventRecord(ev1, s);
+      if ((e = hipEventSynchronize(ev1)) != hipSuccess) break;
+      (void)hipEventElapsedTime(&ms, ev0, ev1);
+      trials.push_back(1000.0 * ms / reps);
+    }
+    if (e != hipSuccess) {
+      result = hip_fail(h, e);
+      break;
+    }
+    const double us = median(trials);
+    if (us < best_us) {
+      best_us = us;
+      best = cand;
+      best.us = us;
+    }
+  }
+  (void)hipEventDestroy(ev0);
+  (void)hipEventDestroy(ev1);
+  if (result != MI_HGEMM_OK) return result;
+  if (best.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
+
+  const Key key{M, N, K, 1};
+  {
+    std::lock_guard<std::mutex> lk(h->mu);
+    h->table[key] = best;
+  }
+  if (flags & MI_HGEMM_TUNE_PERSIST) {
+    if (h->table_path.empty()) return MI_HGEMM_ERR_IO;
+    FILE* f = std::fopen(h->table_path.c_str(), "a");
+    if (!f) return MI_HGEMM_ERR_IO;
+    const bool ok = write_entry(f, key, best);
+    if (std::fclose(f) != 0 || !ok) return MI_HGEMM_ERR_IO;
+  }
+  return MI_HGEMM_OK;
+}

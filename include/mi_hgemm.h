@@ -1,0 +1,166 @@
+/*
+ * mi_hgemm.h -- C ABI of libmi_hgemm, a half-precision GEMM for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation.  For 0 <= i < M and 0 <= j < N:
+ *
+ *     C[i*ldc + j] = fp16_rne( sum_{k=0}^{K-1} A[i*lda + k] * B[j*ldb + k] )
+ *
+ * A is an M x K row-major matrix, B a K x N column-major matrix (stored as N
+ * columns of K contiguous halves), C an M x N row-major matrix; all three hold
+ * IEEE binary16.  Products are accumulated in binary32 on the matrix cores and
+ * the sum is rounded once to binary16, round-to-nearest-even, overflow to
+ * infinity.  alpha = 1 and beta = 0: C is only written.  This is the TN
+ * half-precision GEMM of "RL驱动CUDA L2 GEMM内核自动调优：A100/H100 tile
+ * size与融合优化" (blog.hotdry.top, 2025-12-05), 正文 paragraph 1 (HGEMM) and
+ * paragraph 3 (row-major A, column-major B, the kernel family named ...TN), and
+ * of the per-shape tile/pipeline/swizzle search of "H100 GEMM L2驻留优化：
+ * warp-specialized TMA异步拷贝与RL调优策略" (blog.hotdry.top), 正文 paragraph 4
+ * and 可落地参数清单, which here is mi_hgemm_tune.  In torch terms C = A @ Bt.T
+ * where Bt is the [N, K] storage of B (the nn.Linear weight layout).
+ *
+ * Conventions for every function:
+ *   - Pointers named A, B, C are DEVICE pointers on the handle's device; the
+ *     caller owns them.  Sizes and leading dimensions count elements.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued on it and the call returns without synchronising; a device
+ *     fault surfaces at the caller's next synchronisation.
+ *   - Nothing is allocated per call by mi_hgemm_run.  No exception crosses the
+ *     ABI; every failure is a status code.
+ *   - A handle may be shared by threads calling mi_hgemm_run / mi_hgemm_plan
+ *     concurrently.  mi_hgemm_tune and mi_hgemm_destroy need exclusive use.
+ */
+#ifndef MI_HGEMM_H
+#define MI_HGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MI_HGEMM_VERSION_MAJOR 0
+#define MI_HGEMM_VERSION_MINOR 1
+
+typedef struct mi_hgemm_ctx* mi_hgemm_handle_t;
+
+/* Only the TN layout (A row-major, B column-major) is provided. */
+typedef enum { MI_HGEMM_LAYOUT_TN = 0 } mi_hgemm_layout_t;
+
+typedef enum {
+  MI_HGEMM_OK = 0,
+  MI_HGEMM_ERR_INVALID_ARG = 1,   /* null handle/pointer, negative size, ld too small, C overlapping A or B */
+  MI_HGEMM_ERR_UNSUPPORTED = 2,   /* layout other than TN, a size above INT32_MAX, no instance for the shape */
+  MI_HGEMM_ERR_NO_DEVICE = 3,     /* no gfx950 device (or an inspection-only handle asked to launch) */
+  MI_HGEMM_ERR_HIP = 4,           /* a HIP call failed; see mi_hgemm_last_hip_error */
+  MI_HGEMM_ERR_IO = 5,            /* a table file could not be written */
+  MI_HGEMM_WARN_TABLE_DEFAULTS = 6 /* handle created, but the named table was missing or had bad lines */
+} mi_hgemm_status_t;
+
+/* Flags of mi_hgemm_create_ex. */
+#define MI_HGEMM_CREATE_NO_DEVICE 1u  /* inspection handle: tables and dispatch only, no launches */
+
+/* Flags of mi_hgemm_tune. */
+#define MI_HGEMM_TUNE_EXHAUSTIVE 1u   /* every compiled instance x raster setting (default) */
+#define MI_HGEMM_TUNE_HEURISTIC 2u    /* a pruned candidate list around the built-in choice */
+#define MI_HGEMM_TUNE_PERSIST 4u      /* append the winner to the handle's table file */
+
+/*
+ * Create a handle on the current HIP device.
+ *   table_path: shape->config table to load.  NULL: the path in the
+ *     MI_HGEMM_TABLE environment variable, else the table shipped next to the
+ *     library (tables/gfx950.tsv), else built-in heuristics only.
+ * Returns OK, WARN_TABLE_DEFAULTS (a named table is missing or has malformed
+ * lines: valid lines are kept, heuristics cover the rest), NO_DEVICE (the
+ * current device is not gfx950 or there is none), or INVALID_ARG (out NULL).
+ * On OK and WARN_TABLE_DEFAULTS *out holds a handle to release with
+ * mi_hgemm_destroy; otherwise *out is NULL.
+ */
+mi_hgemm_status_t mi_hgemm_create(mi_hgemm_handle_t* out, const char* table_path);
+
+/* As mi_hgemm_create; with MI_HGEMM_CREATE_NO_DEVICE no device is needed and
+ * the handle supports mi_hgemm_plan and the table functions only. */
+mi_hgemm_status_t mi_hgemm_create_ex(mi_hgemm_handle_t* out, const char* table_path,
+                                     uint32_t flags);
+
+/* Release a handle (NULL is a no-op).  Waits for nothing: the caller must not
+ * destroy a handle whose launches may still read its scratch memory. */
+mi_hgemm_status_t mi_hgemm_destroy(mi_hgemm_handle_t h);
+
+/*
+ * C = A * B as defined at the top of this file, enqueued on `stream`.
+ *   M, N, K >= 0.  M == 0 or N == 0: OK, nothing is done.  K == 0: C is set
+ *   to +0 (beta = 0), by a fill kernel on the stream.
+ *   lda >= max(K,1), ldb >= max(K,1), ldc >= max(N,1).
+ *   A, B, C must be non-NULL when their extent is non-empty, and C's extent
+ *   must not overlap A's or B's (INVALID_ARG).
+ * Alignment: operands in the 16-byte class (A, B, C 16-byte aligned; lda, ldb,
+ * ldc multiples of 8 and at most 2^21; K a multiple of 8) run the vector-load
+ * kernels; anything else runs the element-wise instance with the same
+ * arithmetic.  Misalignment is never an error.
+ * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE or ERR_HIP (launch failed).
+ */
+mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                               const void* A, int64_t lda, const void* B, int64_t ldb,
+                               void* C, int64_t ldc, mi_hgemm_layout_t layout, void* stream);
+
+/*
+ * Search the compiled instances and raster settings for the shape (M, N, K)
+ * in the 16-byte alignment class: each valid candidate is timed with HIP
+ * events on library-owned scratch operands (small integers, so every correct
+ * candidate gives bit-identical C) and checked against the element-wise
+ * instance; the fastest correct one becomes the handle's entry for the shape.
+ * With MI_HGEMM_TUNE_PERSIST the entry is appended to the handle's table file.
+ * Synchronises `stream`.  Allocates scratch (freed before returning).
+ * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
+ */
+mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                mi_hgemm_layout_t layout, void* stream, uint32_t flags);
+
+/* Human-readable name of a status. Never NULL. */
+const char* mi_hgemm_status_string(mi_hgemm_status_t s);
+
+/* The hipError_t of the handle's last failed HIP call (0 if none). */
+int mi_hgemm_last_hip_error(mi_hgemm_handle_t h);
+
+/* Number of compiled kernel instances, and the name of instance `index`
+ * (NULL when out of range).  Instance 0 is the element-wise (any alignment) one. */
+int mi_hgemm_kernel_count(void);
+const char* mi_hgemm_kernel_name(int index);
+
+/*
+ * What mi_hgemm_run would launch for these arguments, without launching:
+ * validates exactly as mi_hgemm_run and writes the instance index, raster
+ * group height and XCD remap flag (any output pointer may be NULL).
+ * *kernel_index is -1 when no kernel would run (empty C, or K == 0).
+ * Works on inspection handles; device pointers are only compared, never read.
+ */
+mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                const void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap);
+
+/*
+ * mi_hgemm_run with a forced instance and raster setting (tests, benchmarks,
+ * external tuners).  Validation as mi_hgemm_run, plus UNSUPPORTED when the
+ * instance needs the 16-byte class and the operands are not in it, or
+ * kernel_index is out of range.  group_m >= 1; xcd_remap 0 or 1.
+ */
+mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
+                                      int32_t group_m, int32_t xcd_remap,
+                                      int64_t M, int64_t N, int64_t K,
+                                      const void* A, int64_t lda, const void* B, int64_t ldb,
+                                      void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                      void* stream);
+
+/* Number of (shape -> config) entries the handle holds. */
+int mi_hgemm_table_size(mi_hgemm_handle_t h);
+
+/* Write the handle's entries to `path` in the table format (ERR_IO on failure). */
+mi_hgemm_status_t mi_hgemm_table_save(mi_hgemm_handle_t h, const char* path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_HGEMM_H */

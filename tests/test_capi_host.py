@@ -1,0 +1,210 @@
+"""Host-side checks of the C ABI (no GPU, no kernel launches).
+
+The library must load and export every function include/mi_hgemm.h declares;
+argument validation, the alignment-class decision, table parsing and dispatch
+are checked through an inspection handle (MI_HGEMM_CREATE_NO_DEVICE), with
+fake device addresses that the library only compares, never dereferences.
+"""
+import os
+import re
+
+import pytest
+import torch
+
+import dense_fp16_gemm_hgemm_amd as mh
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "mi_hgemm.h")
+BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses
+A0, B0, C0 = BASE, BASE + (1 << 36), BASE + (2 << 36)
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mi_hgemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("mi_hgemm_create", "mi_hgemm_run", "mi_hgemm_tune", "mi_hgemm_destroy",
+                 "mi_hgemm_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    import ctypes
+    lib = ctypes.CDLL(mh.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for st in range(7):
+        assert mh.mi_hgemm_status_string(st).startswith("MI_HGEMM_")
+    assert mh.mi_hgemm_status_string(99) == "MI_HGEMM_UNKNOWN_STATUS"
+
+
+def test_kernel_registry():
+    names = mh.kernel_names()
+    assert len(names) == mh.mi_hgemm_kernel_count() > 10
+    assert names[0] == "generic_64x64_w2x2_m32"
+    assert len(set(names)) == len(names)
+    assert mh.mi_hgemm_kernel_name(-1) is None
+    assert mh.mi_hgemm_kernel_name(len(names)) is None
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="a GPU is visible")
+def test_create_without_device_reports_no_device():
+    st, h = mh.mi_hgemm_create()
+    assert st == mh.MI_HGEMM_ERR_NO_DEVICE and h is None
+
+
+@pytest.fixture
+def inspect_handle(tmp_path, monkeypatch):
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    st, h = mh.mi_hgemm_create_ex(str(tmp_path / "absent.tsv"), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_WARN_TABLE_DEFAULTS  # a named table that is missing
+    yield h
+    mh.mi_hgemm_destroy(h)
+
+
+def plan(h, M, N, K, lda=None, ldb=None, ldc=None, A=A0, B=B0, C=C0, layout=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return mh.mi_hgemm_plan(h, M, N, K, A, lda, B, ldb, C, ldc, layout)
+
+
+def test_validation_status_codes(inspect_handle):
+    h = inspect_handle
+    ok, bad, uns = mh.MI_HGEMM_OK, mh.MI_HGEMM_ERR_INVALID_ARG, mh.MI_HGEMM_ERR_UNSUPPORTED
+    assert plan(h, 64, 64, 64)[0] == ok
+    assert plan(h, -1, 64, 64)[0] == bad
+    assert plan(h, 64, -1, 64)[0] == bad
+    assert plan(h, 64, 64, -1)[0] == bad
+    assert plan(h, 64, 64, 64, lda=63)[0] == bad
+    assert plan(h, 64, 64, 64, ldb=63)[0] == bad
+    assert plan(h, 64, 64, 64, ldc=63)[0] == bad
+    assert plan(h, 64, 64, 64, layout=1)[0] == uns
+    assert plan(h, 2 ** 31, 64, 64, lda=64)[0] == uns
+    assert plan(h, 64, 64, 64, A=0)[0] == bad
+    assert plan(h, 64, 64, 64, B=0)[0] == bad
+    assert plan(h, 64, 64, 64, C=0)[0] == bad
+    # C overlapping an operand
+    assert plan(h, 64, 64, 64, C=A0 + 128)[0] == bad
+    assert plan(h, 64, 64, 64, C=B0 + 2 * 64 * 64 - 2)[0] == bad
+    assert plan(h, 64, 64, 64, C=B0 + 2 * 64 * 64)[0] == ok   # adjacent, not overlapping
+    assert mh.mi_hgemm_plan(None, 1, 1, 1, A0, 1, B0, 1, C0, 1)[0] == bad
+
+
+def test_empty_and_k_zero_launch_nothing(inspect_handle):
+    h = inspect_handle
+    assert plan(h, 0, 64, 64, A=0, B=0, C=0) == (mh.MI_HGEMM_OK, -1, 1, 0)
+    assert plan(h, 64, 0, 64, A=0, B=0, C=0, ldc=1)[:2] == (mh.MI_HGEMM_OK, -1)
+    assert plan(h, 64, 0, 64, A=0, B=0, C=0, ldc=0)[0] == mh.MI_HGEMM_ERR_INVALID_ARG
+    assert plan(h, 64, 64, 0, lda=1, ldb=1, A=0, B=0)[:2] == (mh.MI_HGEMM_OK, -1)  # K == 0: fill only
+
+
+def test_inspection_handle_does_not_launch(inspect_handle):
+    h = inspect_handle
+    st = mh.mi_hgemm_run(h, 64, 64, 64, A0, 64, B0, 64, C0, 64)
+    assert st == mh.MI_HGEMM_ERR_NO_DEVICE
+    assert mh.mi_hgemm_run(h, 0, 64, 64, 0, 64, 0, 64, 0, 64) == mh.MI_HGEMM_OK
+    assert mh.mi_hgemm_tune(h, 64, 64, 64) == mh.MI_HGEMM_ERR_NO_DEVICE
+    assert mh.mi_hgemm_run_kernel(h, 0, 1, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_NO_DEVICE
+    assert mh.mi_hgemm_run_kernel(h, 999, 1, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_UNSUPPORTED
+    assert mh.mi_hgemm_run_kernel(h, 0, 0, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_INVALID_ARG
+
+
+def test_misalignment_selects_the_elementwise_instance(inspect_handle):
+    h = inspect_handle
+    generic = 0
+    assert plan(h, 256, 256, 256)[1] != generic
+    assert plan(h, 256, 256, 256, A=A0 + 2)[1] == generic      # A not 16-byte aligned
+    assert plan(h, 256, 256, 256, C=C0 + 8)[1] == generic      # C not 16-byte aligned
+    assert plan(h, 256, 256, 250)[1] == generic                # K not a multiple of 8
+    assert plan(h, 256, 256, 256, lda=260)[1] == generic       # lda not a multiple of 8
+    assert plan(h, 256, 256, 256, ldb=264)[1] != generic       # padded but aligned
+    assert plan(h, 256, 256, 256, ldb=(1 << 21) + 8)[1] == generic  # beyond 32-bit tile offsets
+    aligned_only = mh.mi_hgemm_run_kernel(h, 1, 1, 0, 256, 256, 250, A0, 256, B0, 256, C0, 256)
+    assert aligned_only == mh.MI_HGEMM_ERR_UNSUPPORTED
+
+
+def test_heuristic_picks_by_shape(inspect_handle):
+    h = inspect_handle
+    names = mh.kernel_names()
+    assert names[plan(h, 16, 4096, 4096)[1]].startswith("skinny_")
+    assert names[plan(h, 8192, 8192, 8192)[1]] == "tile_256x256_w2x2_m32"
+    small = names[plan(h, 256, 256, 256)[1]]
+    assert small.startswith("tile_") and small != "tile_256x256_w2x2_m32"
+
+
+def write_table(path, lines):
+    with open(path, "w") as f:
+        f.write("# arch M N K layout align kernel group_m xcd_remap us\n")
+        for ln in lines:
+            f.write(ln + "\n")
+
+
+def test_table_exact_and_nearest_shape(tmp_path, monkeypatch):
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    names = mh.kernel_names()
+    p = tmp_path / "t.tsv"
+    write_table(p, ["gfx950 1000 2000 3000 TN a16 tile_64x64_w2x2_m16 4 1 12.5",
+                    "gfx942 1000 2000 3000 TN a16 tile_32x32_w2x2_m16 1 0 1.0",  # other arch: skipped
+                    "gfx950 512 512 512 TN any generic_64x64_w2x2_m32 2 0 3.0"])
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK
+    try:
+        assert mh.mi_hgemm_table_size(h) == 2
+        r = plan(h, 1000, 2000, 3000)
+        assert names[r[1]] == "tile_64x64_w2x2_m16" and r[2:] == (4, 1)
+        r = plan(h, 1000, 2000, 3000 * 2)                  # one factor of 2 away: nearest entry
+        assert names[r[1]] == "tile_64x64_w2x2_m16"
+        r = plan(h, 1000 * 4, 2000, 3000)                  # too far: heuristics
+        assert names[r[1]] != "tile_64x64_w2x2_m16"
+        r = plan(h, 512, 512, 512, lda=516)                # unaligned class entry
+        assert r[1:] == (0, 2, 0)
+        out = tmp_path / "saved.tsv"
+        assert mh.mi_hgemm_table_save(h, str(out)) == mh.MI_HGEMM_OK
+        st2, h2 = mh.mi_hgemm_create_ex(str(out), mh.MI_HGEMM_CREATE_NO_DEVICE)
+        assert st2 == mh.MI_HGEMM_OK and mh.mi_hgemm_table_size(h2) == 2
+        mh.mi_hgemm_destroy(h2)
+        assert mh.mi_hgemm_table_save(h, str(tmp_path / "no" / "dir.tsv")) == mh.MI_HGEMM_ERR_IO
+    finally:
+        mh.mi_hgemm_destroy(h)
+
+
+def test_corrupt_table_warns_and_keeps_good_lines(tmp_path, monkeypatch):
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    p = tmp_path / "bad.tsv"
+    write_table(p, ["gfx950 1000 2000 3000 TN a16 tile_64x64_w2x2_m16 4 1 12.5",
+                    "gfx950 not a number",
+                    "gfx950 64 64 64 TN a16 no_such_kernel 1 0 1.0",
+                    "gfx950 64 64 64 TN any tile_128x128_w2x2_m32 1 0 1.0",  # aligned kernel in 'any'
+                    "gfx950 64 64 64 TN a16 tile_32x32_w2x2_m16 0 0 1.0"])   # group_m < 1
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_WARN_TABLE_DEFAULTS
+    assert mh.mi_hgemm_table_size(h) == 1
+    mh.mi_hgemm_destroy(h)
+
+
+def test_table_from_environment(tmp_path, monkeypatch):
+    p = tmp_path / "env.tsv"
+    write_table(p, ["gfx950 64 64 64 TN a16 tile_32x32_w2x2_m16 1 0 1.0"])
+    monkeypatch.setenv("MI_HGEMM_TABLE", str(p))
+    st, h = mh.mi_hgemm_create_ex(None, mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK and mh.mi_hgemm_table_size(h) == 1
+    mh.mi_hgemm_destroy(h)
+
+
+def test_create_rejects_null_out():
+    import ctypes
+    lib = ctypes.CDLL(mh.LIB_PATH)
+    lib.mi_hgemm_create.restype = ctypes.c_int
+    lib.mi_hgemm_create.argtypes = [ctypes.c_void_p, ctypes.c_char_p]
+    assert lib.mi_hgemm_create(None, None) == mh.MI_HGEMM_ERR_INVALID_ARG

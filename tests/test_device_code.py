@@ -1,0 +1,51 @@
+"""Every registered kernel instance has device code for gfx950 in libmi_hgemm.so.
+
+Host-only check: the .hip_fatbin section of the library is unbundled with the
+ROCm clang-offload-bundler and its symbol table read with llvm-readelf.  A
+registry entry whose kernel template was never instantiated in the device pass
+would otherwise only show up as a launch failure on the GPU.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import dense_fp16_gemm_hgemm_amd as mh
+
+LLVM = "/opt/rocm/lib/llvm/bin"
+
+
+def mangled(name):
+    m = re.fullmatch(r"(tile|generic)_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
+    if m:
+        kind, bm, bn, wm, wn, mf = m.groups()
+        tmpl = f"{len(kind) + 7}{kind}_kernel"
+        return f"_ZN4mihg{tmpl}ILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)", name)
+    if m:
+        fm, fn, w, u = m.groups()
+        return f"_ZN4mihg13skinny_kernelILi{fm}ELi{fn}ELi{w}ELi{u}EEEvNS_8GemmArgsE"
+    raise AssertionError(f"unrecognised kernel name {name}")
+
+
+@pytest.mark.skipif(not (shutil.which("objcopy") and os.path.exists(LLVM + "/llvm-readelf")),
+                    reason="binutils / ROCm llvm tools not available")
+def test_every_registered_kernel_has_gfx950_code(tmp_path):
+    fat = tmp_path / "fat.bin"
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", mh.LIB_PATH,
+                    str(tmp_path / "copy.so")], check=True)
+    targets = subprocess.run([LLVM + "/clang-offload-bundler", "--list", "--type=o",
+                              f"--input={fat}"], check=True, capture_output=True,
+                             text=True).stdout.split()
+    gfx = [t for t in targets if t.endswith("gfx950")]
+    assert gfx, f"no gfx950 code object in the library: {targets}"
+    co = tmp_path / "dev.co"
+    subprocess.run([LLVM + "/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    f"--targets={gfx[0]}", f"--output={co}"], check=True)
+    syms = subprocess.run([LLVM + "/llvm-readelf", "-s", "-W", str(co)], check=True,
+                          capture_output=True, text=True).stdout
+    have = set(re.findall(r"(_ZN4mihg\S+)", syms))
+    missing = [n for n in mh.kernel_names() if mangled(n) not in have]
+    assert not missing, f"kernels without device code: {missing}"

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Every case draws seeded inputs from dense_fp16_gemm_hgemm_amd.inputs, runs the
+GPU library, copies C back and compares with the oracle (tests/parity.py for
+the rules).  Sizes the oracle finishes in seconds are compared element by
+element; the full benchmark sizes are compared on sampled elements.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import check_bitexact, check_tolerance, sample_indices
+
+pytestmark = pytest.mark.gpu
+
+mh = pytest.importorskip("dense_fp16_gemm_hgemm_amd")
+from dense_fp16_gemm_hgemm_amd import inputs  # noqa: E402
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+DEV = torch.device("cuda", 0)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    h = mh.Hgemm()
+    yield h
+    h.close()
+
+
+def gpu(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def padded_out(M, N):
+    """C with ldc rounded up to a multiple of 8 (the 16-byte class), NaN-filled."""
+    ldc = (N + 7) // 8 * 8
+    return torch.full((M, ldc), float("nan"), dtype=torch.float16, device=DEV)[:, :N]
+
+
+def rand_problem(M, N, K, kind="randn", seed=0, scale=None):
+    s = (1.0 / np.sqrt(K)) if scale is None else scale
+    p = inputs.Problem(f"case_{M}x{N}x{K}", M, N, K, kind, s, s, seed)
+    return inputs.make(p)
+
+
+SMALL_SHAPES = [(64, 64, 64), (100, 130, 72), (17, 33, 40), (256, 256, 512), (300, 520, 1000),
+                (1, 8, 8), (16, 4096, 256), (64, 200, 2048)]
+
+
+@pytest.fixture(scope="module")
+def small_cases():
+    cases = {}
+    for (M, N, K) in SMALL_SHAPES:
+        for kind in ("randn", "int"):
+            A, Bt = rand_problem(M, N, K, kind, seed=M * 7 + N * 3 + K)
+            cases[(M, N, K, kind)] = (A, Bt, oracle.hgemm_tn(A, Bt))
+    return cases
+
+
+@pytest.mark.parametrize("kidx", range(len(mh.kernel_names())), ids=mh.kernel_names())
+def test_every_instance_small_shapes(lib, small_cases, kidx):
+    name = mh.kernel_names()[kidx]
+    rasters = [(1, 0), (8, 1), (3, 1)] if name.startswith("tile_") else [(1, 0)]
+    for (M, N, K, kind), (A, Bt, ref) in small_cases.items():
+        dA, dB = gpu(A), gpu(Bt)
+        for gm, xcd in rasters:
+            log(f"{name} {M}x{N}x{K} {kind} raster=({gm},{xcd})")
+            out = padded_out(M, N)
+            lib.run_kernel(kidx, dA, dB, out, group_m=gm, xcd_remap=xcd)
+            got = host(out)
+            what = f"{name} {M}x{N}x{K} {kind} raster=({gm},{xcd})"
+            if kind == "int":
+                check_bitexact(got, ref, what)
+            else:
+                check_tolerance(got, ref, what)
+
+
+def test_tiny_config_full(lib):
+    p = inputs.tiny()
+    A, Bt = inputs.make(p)
+    log(f"{p.name}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    check_tolerance(got, oracle.hgemm_tn(A, Bt), p.name)
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["randn", "int"])
+def test_small_config_full(lib, integer):
+    p = inputs.small(integer)
+    A, Bt = inputs.make(p)
+    log(f"{p.name}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    ref = oracle.hgemm_tn(A, Bt)
+    if integer:
+        check_bitexact(got, ref, p.name)
+    else:
+        check_tolerance(got, ref, p.name)
+
+
+@pytest.mark.parametrize("p", inputs.llm(), ids=lambda p: p.name)
+def test_llm_configs(lib, p):
+    A, Bt = inputs.make(p)
+    log(f"{p.name}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    if p.M <= 64:
+        check_tolerance(got, oracle.hgemm_tn(A, Bt), p.name)
+    else:
+        r, c = sample_indices(p.M, p.N, 4096, seed=p.seed)
+        check_tolerance(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
+
+
+@pytest.mark.slow
+def test_square_8192_sampled(lib):
+    p = inputs.square()
+    A, Bt = inputs.make(p)
+    log(f"{p.name}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    r, c = sample_indices(p.M, p.N, 8192, seed=6)
+    check_tolerance(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
+
+
+INT_SHAPES = [(64, 4096, 64), (128, 2048, 128), (16, 4096, 4096), (64, 11008, 4096),
+              (256, 4096, 11008), (1024, 14336, 4096), (8192, 8192, 8192)]
+
+
+@pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_integer_variant_bitexact_every_config_shape(lib, shape):
+    """U{-4..4} inputs: every partial sum is an integer below 2^24 in magnitude,
+    so fp32 accumulation is exact and the result must equal the oracle bit for bit."""
+    M, N, K = shape
+    A, Bt = rand_problem(M, N, K, "int", seed=3 + M + N + K)
+    log(f"int {M}x{N}x{K}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    if M * N * K <= 64 * 4096 * 4096:
+        check_bitexact(got, oracle.hgemm_tn(A, Bt), f"int {shape}")
+    else:
+        r, c = sample_indices(M, N, 4096, seed=M)
+        check_bitexact(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), f"int {shape}")
+
+
+@pytest.mark.parametrize("kind,M", [("identity", 128), ("identity", 256), ("perm", 128),
+                                    ("perm", 256)])
+def test_identity_and_permutation_bitexact(lib, kind, M):
+    p = inputs.Problem(f"{kind}{M}", M, 2048, M, kind, seed=M)
+    A, Bt = inputs.make(p)
+    log(p.name)
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    check_bitexact(got, oracle.hgemm_tn(A, Bt), p.name)
+
+
+def test_k_zero_writes_zeros(lib):
+    A = torch.empty((5, 0), dtype=torch.float16, device=DEV)
+    Bt = torch.empty((7, 0), dtype=torch.float16, device=DEV)
+    out = torch.full((5, 7), float("nan"), dtype=torch.float16, device=DEV)
+    lib.run(A, Bt, out)
+    got = host(out)
+    assert np.array_equal(got.view(np.uint16), np.zeros((5, 7), np.uint16))
+
+
+def test_empty_output_is_a_no_op(lib):
+    A = torch.ones((0, 16), dtype=torch.float16, device=DEV)
+    Bt = torch.ones((8, 16), dtype=torch.float16, device=DEV)
+    assert lib.run(A, Bt).shape == (0, 8)
+
+
+@pytest.mark.parametrize("M,N,K,pad_a,pad_b,pad_c,off", [
+    (1, 1, 1, 0, 0, 0, 0),
+    (33, 45, 70, 5, 3, 1, 0),      # K not a multiple of 8 and odd leading dims: element-wise path
+    (64, 64, 64, 0, 0, 0, 1),      # operands offset by one element: misaligned
+    (96, 130, 136, 8, 16, 6, 0),   # padded, aligned ld; N tail not a multiple of 4 in C
+    (128, 128, 4104, 0, 0, 0, 0),  # K tail beyond a 64-multiple
+    (48, 1000, 8, 0, 0, 0, 0),     # minimal K for the vector path
+])
+def test_edge_shapes_and_layouts(lib, M, N, K, pad_a, pad_b, pad_c, off):
+    A, Bt = rand_problem(M, N, K, "randn", seed=K)
+    ref = oracle.hgemm_tn(A, Bt)
+    log(f"edge {M}x{N}x{K} pads=({pad_a},{pad_b},{pad_c}) off={off}")
+    bigA = torch.zeros(M * (K + pad_a) + off + 8, dtype=torch.float16, device=DEV)
+    bigB = torch.zeros(N * (K + pad_b) + off + 8, dtype=torch.float16, device=DEV)
+    bigC = torch.full((M * (N + pad_c) + off + 8,), 7.0, dtype=torch.float16, device=DEV)
+    dA = bigA[off:off + M * (K + pad_a)].view(M, K + pad_a)[:, :K]
+    dB = bigB[off:off + N * (K + pad_b)].view(N, K + pad_b)[:, :K]
+    dC = bigC[off:off + M * (N + pad_c)].view(M, N + pad_c)[:, :N]
+    dA.copy_(gpu(A))
+    dB.copy_(gpu(Bt))
+    lib.run(dA, dB, dC)
+    got = host(dC)
+    check_tolerance(got, ref, f"edge {M}x{N}x{K}")
+    full = host(bigC)
+    mask = np.ones(full.shape, bool)
+    view = np.arange(full.size)[off:off + M * (N + pad_c)].reshape(M, N + pad_c)[:, :N]
+    mask[view.ravel()] = False
+    assert np.all(full[mask] == np.float16(7.0)), "elements outside C were written"
+
+
+def test_integer_ragged_bitexact_all_paths(lib):
+    A, Bt = rand_problem(77, 93, 200, "int", seed=5)
+    ref = oracle.hgemm_tn(A, Bt)
+    for kidx, name in enumerate(mh.kernel_names()):
+        log(f"ragged int {name}")
+        got = host(lib.run_kernel(kidx, gpu(A), gpu(Bt), padded_out(77, 93)))
+        check_bitexact(got, ref, name)
+
+
+def test_subnormal_inputs(lib):
+    rng = np.random.default_rng(21)
+    A = (rng.standard_normal((128, 512)) * 1e-4).astype(np.float16)   # many subnormal
+    Bt = (rng.standard_normal((256, 512)) * 3.0).astype(np.float16)
+    assert np.count_nonzero(np.abs(A) < 2.0 ** -14) > 1000
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    check_tolerance(got, oracle.hgemm_tn(A, Bt), "subnormal inputs")
+
+
+def test_overflow_to_infinity(lib):
+    A = np.full((64, 64), 64.0, dtype=np.float16)
+    Bt = np.full((64, 64), 32.0, dtype=np.float16)    # 64*64*32 = 131072 > 65504
+    Bt[1::2] = -Bt[1::2]
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    check_bitexact(got, oracle.hgemm_tn(A, Bt), "overflow")
+
+
+def test_deterministic(lib):
+    A, Bt = rand_problem(512, 1024, 2048, "randn", seed=9)
+    dA, dB = gpu(A), gpu(Bt)
+    first = host(lib.run(dA, dB)).view(np.uint16).copy()
+    for _ in range(3):
+        assert np.array_equal(host(lib.run(dA, dB)).view(np.uint16), first)
+
+
+def test_runs_on_a_side_stream(lib):
+    A, Bt = rand_problem(256, 384, 512, "int", seed=11)
+    ref = oracle.hgemm_tn(A, Bt)
+    s = torch.cuda.Stream()
+    dA, dB = gpu(A), gpu(Bt)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = lib.run(dA, dB, stream=s)
+    s.synchronize()
+    check_bitexact(out.cpu().numpy(), ref, "side stream")
+
+
+def test_invalid_arguments_raise(lib):
+    A = torch.ones((4, 8), dtype=torch.float16, device=DEV)
+    Bt = torch.ones((4, 8), dtype=torch.float16, device=DEV)
+    st = mh.mi_hgemm_run(lib.handle, 4, 4, 8, A.data_ptr(), 4, Bt.data_ptr(), 8,
+                         torch.empty(16, dtype=torch.float16, device=DEV).data_ptr(), 4)
+    assert st == mh.MI_HGEMM_ERR_INVALID_ARG   # lda < K
+    st = mh.mi_hgemm_run(lib.handle, 4, 4, 8, A.data_ptr(), 8, Bt.data_ptr(), 8,
+                         A.data_ptr(), 4)
+    assert st == mh.MI_HGEMM_ERR_INVALID_ARG   # C overlaps A
+    with pytest.raises(mh.HgemmError) as ei:
+        lib.tune(64, 64, 60)                   # K % 8 != 0: nothing to tune
+    assert ei.value.status == mh.MI_HGEMM_ERR_UNSUPPORTED
+
+
+def test_tuner_builds_a_table_entry(tmp_path):
+    table = tmp_path / "tuned.tsv"
+    h = mh.Hgemm(str(table))
+    assert h.create_status == mh.MI_HGEMM_WARN_TABLE_DEFAULTS
+    log("tune 192x640x320")
+    h.tune(192, 640, 320, mh.MI_HGEMM_TUNE_EXHAUSTIVE | mh.MI_HGEMM_TUNE_PERSIST)
+    assert h.table_size() == 1
+    lines = [ln for ln in table.read_text().splitlines() if not ln.startswith("#")]
+    assert len(lines) == 1 and lines[0].startswith("gfx950 192 640 320 TN a16 ")
+    A, Bt = rand_problem(192, 640, 320, "randn", seed=4)
+    dA, dB = gpu(A), gpu(Bt)
+    name, _, _ = h.plan(dA, dB)
+    assert name == lines[0].split()[6]
+    check_tolerance(host(h.run(dA, dB)), oracle.hgemm_tn(A, Bt), "tuned")
+    h2 = mh.Hgemm(str(table))
+    assert h2.create_status == mh.MI_HGEMM_OK and h2.table_size() == 1
+    h.close()
+    h2.close()
