@@ -20,6 +20,9 @@ namespace mihg {
 #define MIHG_TILE_INSTANCES(X) \
   X(256, 256, 2, 2, 32)          \
   X(256, 256, 2, 4, 32)          \
+  X(256, 256, 2, 2, 16)          \
+  X(256, 256, 2, 4, 16)          \
+  X(128, 128, 2, 2, 16)          \
   X(256, 128, 2, 2, 32)          \
   X(128, 256, 2, 2, 32)          \
   X(256, 128, 4, 2, 32)          \
@@ -32,6 +35,18 @@ namespace mihg {
   X(64, 32, 4, 1, 16)            \
   X(32, 32, 2, 2, 16)            \
   X(16, 64, 1, 2, 16)
+
+#define MIHG_DTILE_INSTANCES(X) \
+  X(256, 256, 2, 2, 16, 4)        \
+  X(256, 256, 2, 4, 16, 4)        \
+  X(256, 128, 2, 2, 16, 4)        \
+  X(128, 256, 2, 2, 16, 4)        \
+  X(128, 128, 2, 2, 16, 4)
+
+#define MIHG_D2TILE_INSTANCES(X) \
+  X(256, 256, 2, 4)               \
+  X(256, 128, 2, 2)               \
+  X(128, 128, 2, 2)
 
 #define MIHG_SKINNY_INSTANCES(X) \
   X(1, 1, 4, 4)                  \
@@ -47,10 +62,16 @@ namespace mihg {
 
 #define INSTANTIATE_TILE(BM, BN, WGM, WGN, MF) \
   template __global__ void tile_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
+#define INSTANTIATE_DTILE(BM, BN, WGM, WGN, MF, S) \
+  template __global__ void dtile_kernel<BM, BN, WGM, WGN, MF, S>(GemmArgs);
+#define INSTANTIATE_D2TILE(BM, BN, WGM, WGN) \
+  template __global__ void d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_SKINNY(FM, FN, W, U) \
   template __global__ void skinny_kernel<FM, FN, W, U>(GemmArgs);
 template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
 MIHG_TILE_INSTANCES(INSTANTIATE_TILE)
+MIHG_DTILE_INSTANCES(INSTANTIATE_DTILE)
+MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 
 // The registry holds host launch functions, so it exists only in the host pass.
@@ -58,6 +79,13 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 #define TILE_DESC(BM, BN, WGM, WGN, MF)                                                     \
   {"tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, 1, 1, \
    2 * (BM + BN) * kLdsRow * 2, &launch_tile<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
+#define DTILE_DESC(BM, BN, WGM, WGN, MF, S)                                             \
+  {"dtile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF "_s" #S, FAMILY_TILE, BM, BN, 32,       \
+   WGM * WGN, MF, 1, 1, 4 * (BM + BN) * kDRow * 2, &launch_dtile<BM, BN, WGM, WGN, MF, S>, \
+   &grid_tile<BM, BN>},
+#define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
+  {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
+   1, 2 * (BM + BN) * kD2Row * 2, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
 #define SKINNY_DESC(FM, FN, W, U)                                                          \
   {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
    W * 16 * FM * 16 * FN * 4, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
@@ -67,6 +95,8 @@ const KernelDesc kKernels[] = {
     {"generic_64x64_w2x2_m32", FAMILY_TILE, 64, 64, 64, 4, 32, 0, 1, 128 * 64 * 2,
      &launch_generic<64, 64, 2, 2, 32>, &grid_tile<64, 64>},
     MIHG_TILE_INSTANCES(TILE_DESC)
+    MIHG_DTILE_INSTANCES(DTILE_DESC)
+    MIHG_D2TILE_INSTANCES(D2TILE_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
 };
 

@@ -32,6 +32,8 @@
 // output row, which makes the C stores 8-byte vectors along N.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mihg {
@@ -350,6 +352,514 @@ tile_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct-to-LDS tile family ("dtile"): BM x BN x 32 K tiles loaded by
+// buffer_load_dwordx4 ... lds (global -> LDS without passing through VGPRs)
+// into a ring of S LDS stages, one wave per SIMD, large wave tiles.
+//
+// LDS layout: 64-byte rows (32 halves, 4 chunks of 16 bytes), chunk index
+// XORed with (row >> 2) & 3.  One DMA instruction of a wave fills a 1 KiB
+// block = 16 rows; lane l lands on row l/4, physical chunk l%4, so it loads
+// logical chunk (l%4) ^ (l/16) -- the same for every block, one offset
+// register per operand.  A 16-row fragment read at one logical chunk touches
+// 16 distinct (row mod 4, chunk) bank groups: conflict-free with 64 banks.
+//
+// Pipeline (trip k): issue the DMA of tile k+S-1 into the stage tile k-1 used;
+// read tile k+1's fragments (published one barrier ago) into the second
+// register set; run tile k's MFMAs; wait until tile k+2's DMA has landed
+// (this wave's part), and barrier.  The DMA of a tile therefore has S-2 trips
+// to arrive, and the MFMAs of trip k+1 start right after the barrier.  Each
+// stage is its own LDS object and trips are unrolled so stage and register
+// indices are constants, which lets the compiler tell the in-flight DMA
+// apart from the fragment reads instead of waiting for every DMA.
+constexpr int kDRow = 32;  // halves per LDS row (no padding; XOR swizzle)
+
+// Raw buffer descriptor as four dwords (base, base_hi | stride 0, records, word3).
+__device__ inline u32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = (uint32_t)a;
+  r[1] = (uint32_t)(a >> 32) & 0xffffu;
+  r[2] = bytes;
+  r[3] = (uint32_t)kRsrcWord3;
+  return r;
+}
+// LDS byte address of a __shared__ object (the low half of its flat address).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uint64_t>(p);
+}
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane l's 16 bytes at
+// voff + soff (bounded by the descriptor; out of range reads 0) land at LDS
+// byte address lds + 16 * l.
+__device__ inline void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+template <int BM, int BN>
+struct DStages {
+  static constexpr int kStage = (BM + BN) * kDRow;
+  _Float16 s0[kStage], s1[kStage], s2[kStage], s3[kStage];
+};
+
+template <int I, int BM, int BN>
+__device__ __forceinline__ _Float16* dstage(DStages<BM, BN>& d) {
+  if constexpr (I == 0) return d.s0;
+  else if constexpr (I == 1) return d.s1;
+  else if constexpr (I == 2) return d.s2;
+  else return d.s3;
+}
+
+// Spread the trip's ND copies and NR fragment reads evenly over its first
+// three quarters of MFMAs: four waves issuing reads back to back ask the LDS
+// for about twice its bandwidth, and a read issued near the end of the trip
+// makes the wave wait for it at the barrier.  The last quarter is MFMA only.
+template <int NM, int ND, int NR>
+__device__ __forceinline__ void dtrip_schedule() {
+  constexpr int SPAN = (NM * 3) / 4;
+  constexpr int NX = ND + NR;
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    // memory slot x is placed after MFMA floor(x * SPAN / NX)
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+      if (x * SPAN / NX == i) {
+        // copies first (slots 0, 2, 4, ...), reads fill the rest
+        const bool is_copy = (x % 2 == 0) && (x / 2 < ND);
+        if (is_copy) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+dtile_kernel(GemmArgs p) {
+  using MM = Mfma<MF>;
+  constexpr int BK = 32;
+  constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int KSTEPS = BK / MM::KI;
+  constexpr int A_BLK = BM / 16 / NW, B_BLK = BN / 16 / NW;  // 1 KiB DMA blocks per wave
+  constexpr int ND = A_BLK + B_BLK;
+  constexpr int U = (S % 2 == 0) ? S : 2 * S;  // trips per unrolled loop body
+  static_assert(S == 4, "four LDS stages");
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "DMA blocks must split evenly");
+  static_assert(FM % 4 == 0 || MF == 32 || true, "");
+
+  __shared__ __attribute__((aligned(1024))) DStages<BM, BN> lds;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+  // DMA: lane -> (row l/4 of a 16-row block, logical chunk (l%4)^(l/16)).
+  // The copy is issued by inline asm: the compiler then does not treat it as
+  // an LDS store, so the workgroup barrier's fence does not drain every copy
+  // in flight; completion is tracked explicitly with vmcnt (wait_dma).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int drow = lane >> 2, dchunk = (lane & 3) ^ (lane >> 4);
+  const uint32_t a_voff = (uint32_t)(drow * lda * 2 + dchunk * 16);
+  const uint32_t b_voff = (uint32_t)(drow * ldb * 2 + dchunk * 16);
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const bool mask_k = (K & 31) != 0;
+  auto dma = [&](_Float16* stage, int k0) {
+    const uint32_t kb = (uint32_t)k0 * 2;
+    const bool kin = !mask_k || (k0 + dchunk * 8 < K);
+    const uint32_t av = kin ? a_voff : kOOB, bv = kin ? b_voff : kOOB;
+    const uint32_t sbase = lds_addr(stage);
+#pragma unroll
+    for (int i = 0; i < A_BLK; ++i) {
+      const int blk = wave_u * A_BLK + i;
+      dma16(rda, av, (uint32_t)(blk * 16 * lda * 2) + kb, sbase + blk * 16 * kDRow * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < B_BLK; ++i) {
+      const int blk = wave_u * B_BLK + i;
+      dma16(rdb, bv, (uint32_t)(blk * 16 * ldb * 2) + kb, sbase + (BM + blk * 16) * kDRow * 2);
+    }
+  };
+
+  // copy number x of a trip: A blocks first, then B blocks
+  auto dma_one = [&](_Float16* stage, int k0, int x) {
+    const uint32_t kb = (uint32_t)k0 * 2;
+    const bool kin = !mask_k || (k0 + dchunk * 8 < K);
+    const uint32_t sbase = lds_addr(stage);
+    if (x < A_BLK) {
+      const int blk = wave_u * A_BLK + x;
+      dma16(rda, kin ? a_voff : kOOB, (uint32_t)(blk * 16 * lda * 2) + kb,
+            sbase + blk * 16 * kDRow * 2);
+    } else {
+      const int blk = wave_u * B_BLK + (x - A_BLK);
+      dma16(rdb, kin ? b_voff : kOOB, (uint32_t)(blk * 16 * ldb * 2) + kb,
+            sbase + (BM + blk * 16) * kDRow * 2);
+    }
+  };
+
+  // fragment reads: row base + per-lane physical chunk; fm / fn / step are immediates
+  const int frow = lane % MF, fq = lane / MF;
+  int fa_off[KSTEPS], fb_off[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int q = s * (MM::KI / 8) + fq;            // logical chunk
+    const int phys = q ^ ((frow >> 2) & 3);          // block bases are multiples of 16 rows
+    fa_off[s] = (wm * WTM + frow) * kDRow + phys * 8;
+    fb_off[s] = (BM + wn * WTN + frow) * kDRow + phys * 8;
+  }
+  h8 fa[2][KSTEPS][FM], fb[2][KSTEPS][FN];
+  auto fread = [&](const _Float16* stage, int buf) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        fa[buf][s][fm] = *reinterpret_cast<const h8*>(stage + fa_off[s] + fm * MF * kDRow);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        fb[buf][s][fn] = *reinterpret_cast<const h8*>(stage + fb_off[s] + fn * MF * kDRow);
+    }
+  };
+
+  // fragment read number r of a tile: per step, the FM A fragments then the FN B fragments
+  auto fread_one = [&](const _Float16* stage, int buf, int r) {
+    const int s = r / (FM + FN), q = r % (FM + FN);
+    if (q < FM)
+      fa[buf][s][q] = *reinterpret_cast<const h8*>(stage + fa_off[s] + q * MF * kDRow);
+    else
+      fb[buf][s][q - FM] =
+          *reinterpret_cast<const h8*>(stage + fb_off[s] + (q - FM) * MF * kDRow);
+  };
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = MM::mma(fb[buf][s][fn], fa[buf][s][fm], acc[fm][fn]);
+  };
+  // vmcnt(n) with the other counters left alone (gfx9 encoding)
+  auto wait_dma = [&]() {
+    constexpr int n = ND * (S - 3);
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  // prologue: tiles 0 .. S-2 in flight; tiles 0 and 1 published
+  dma(dstage<0>(lds), 0);
+  dma(dstage<1>(lds), BK);
+  if constexpr (S == 4) dma(dstage<2>(lds), 2 * BK);
+  wait_dma();
+  __syncthreads();
+  fread(dstage<0>(lds), 0);
+
+  // trip J of the unrolled body handles tile kt + J: stage (J % S), buffers J & 1.
+  // The trip is written out as an explicit order of slots: slot i issues MFMA
+  // i, then possibly one copy or one fragment read of the next tile.  Copies
+  // and reads are spread over the first three quarters of the trip (four
+  // waves reading back to back would ask the LDS for twice its bandwidth);
+  // the last quarter is MFMA only, so no wait is left for the barrier.  The
+  // scheduler is not allowed to reorder slots: the copies are inline asm it
+  // cannot place, and a block of them at the top of the trip idles the matrix
+  // pipe.
+  auto trip = [&](auto JC, int kt) {
+    constexpr int J = decltype(JC)::value;
+    constexpr int SN = (J + 1) % S, SW = (J + S - 1) % S;
+    constexpr int BUF = J & 1, NB = BUF ^ 1;
+    constexpr int NM = FM * FN * KSTEPS, NR = (FM + FN) * KSTEPS, NX = ND + NR;
+    constexpr int SPAN = (NM * 3) / 4;
+    _Float16* wst = dstage<SW>(lds);
+    const _Float16* rst = dstage<SN>(lds);
+    const int kw = (kt + S - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int s = i / (FM * FN), fm = (i / FN) % FM, fn = i % FN;
+      acc[fm][fn] = MM::mma(fb[BUF][s][fn], fa[BUF][s][fm], acc[fm][fn]);
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        if (x * SPAN / NX != i) continue;
+        // the first 2*ND slots alternate copy / read, the rest are reads
+        if (x < 2 * ND) {
+          if (x % 2 == 0) dma_one(wst, kw, x / 2);
+          else fread_one(rst, NB, x / 2);
+        } else {
+          fread_one(rst, NB, x - ND);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_dma();
+    __syncthreads();
+  };
+  for (int kt = 0; kt < nk; kt += U) {
+    trip(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) trip(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) trip(std::integral_constant<int, 2>{}, kt + 2);
+    if constexpr (U > 3) {
+      if (kt + 3 < nk) trip(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    if constexpr (U > 4) {
+      if (kt + 4 < nk) trip(std::integral_constant<int, 4>{}, kt + 4);
+      if (kt + 5 < nk) trip(std::integral_constant<int, 5>{}, kt + 5);
+    }
+  }
+  // drain the DMA still in flight before the workgroup exits
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
+
+  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          h4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][4 * g + e];
+          buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                       (_Float16)acc[fm][fn][4 * g + e]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-stage direct-to-LDS family ("d2tile"): BM x BN x 64 K tiles, one wave
+// per SIMD, the K tile split into two MFMA steps of 32 that are software
+// pipelined across the barrier.
+//
+// A barrier costs the single wave on each SIMD its matrix pipe for the whole
+// round trip, so the trip is made long: each one holds 2 x FM x FN MFMAs.
+// Trip k (between two barriers):
+//   first half : MFMAs of step 1 of tile k-1 (fragments read last trip), while
+//                tile k+1 is copied into the other stage and the step-0
+//                fragments of tile k (published by the barrier just passed)
+//                are read;
+//   second half: MFMAs of step 0 of tile k, while the step-1 fragments of tile
+//                k are read;
+//   then the wave waits for its copies of tile k+1 and the barrier publishes it.
+// LDS rows are 128 bytes (64 halves, 8 chunks), chunk XORed with (row>>1)&7:
+// 16 consecutive rows read at one logical chunk fall on 16 distinct (row
+// parity, chunk) bank groups of a 64-bank LDS.  A copy instruction fills 8
+// rows; its lanes need one of two global offsets (even or odd block).
+constexpr int kD2Row = 64;  // halves per LDS row
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+d2tile_kernel(GemmArgs p) {
+  using MM = Mfma<16>;
+  constexpr int MF = 16, BK = 64, KSTEPS = 2;
+  constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int A_BLK = BM / 8 / NW, B_BLK = BN / 8 / NW;  // 1 KiB copies per wave
+  constexpr int ND = A_BLK + B_BLK;
+  constexpr int STAGE = (BM + BN) * kD2Row;
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy blocks must split evenly");
+  static_assert(A_BLK % 2 == 0 && B_BLK % 2 == 0, "blocks pair up by parity");
+
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+  // copies: lane l -> row l/8 of an 8-row block, physical chunk l%8, which
+  // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int drow = lane >> 3;
+  const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const uint32_t a_v0 = (uint32_t)(drow * lda * 2 + dch0 * 16), a_v1 = (uint32_t)(drow * lda * 2 + dch1 * 16);
+  const uint32_t b_v0 = (uint32_t)(drow * ldb * 2 + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * 2 + dch1 * 16);
+  const bool mask_k = (K & 63) != 0;
+  const uint32_t lds0 = lds_addr(lds);
+  // copy x (0..ND-1) of tile k0 into stage st
+  auto dma_one = [&](int st, int k0, int x) {
+    const uint32_t kb = (uint32_t)k0 * 2;
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
+    if (x < A_BLK) {
+      const int blk = wave_u * A_BLK + x;
+      const int ch = (x & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (k0 + ch * 8 < K);
+      dma16(rda, kin ? ((x & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
+            sbase + blk * 8 * kD2Row * 2);
+    } else {
+      const int xb = x - A_BLK;
+      const int blk = wave_u * B_BLK + xb;
+      const int ch = (xb & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (k0 + ch * 8 < K);
+      dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
+            sbase + (BM + blk * 8) * kD2Row * 2);
+    }
+  };
+
+  // fragments: row base + per-lane physical chunk of logical chunk 4s + l/16
+  const int frow = lane % MF, fq = lane / MF, fsw = (frow >> 1) & 7;
+  int fa_off[KSTEPS], fb_off[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int phys = (4 * s + fq) ^ fsw;
+    fa_off[s] = (wm * WTM + frow) * kD2Row + phys * 8;
+    fb_off[s] = (BM + wn * WTN + frow) * kD2Row + phys * 8;
+  }
+  h8 fa[2][FM], fb[2][FN];  // [step]
+  auto fread_one = [&](int st, int s, int r) {
+    const _Float16* base = lds + st * STAGE;
+    if (r < FM)
+      fa[s][r] = *reinterpret_cast<const h8*>(base + fa_off[s] + r * MF * kD2Row);
+    else
+      fb[s][r - FM] = *reinterpret_cast<const h8*>(base + fb_off[s] + (r - FM) * MF * kD2Row);
+  };
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  constexpr int NM = FM * FN, NR = FM + FN;
+  // One half trip: the NM MFMAs of step S_MFMA (when DO_MFMA), with the
+  // copies of the next tile (when COPY) and the NR fragment reads of step
+  // S_READ spread over its first three quarters; copies and reads alternate
+  // while copies last.
+  auto half = [&](auto DO_MFMA, auto COPY, auto S_MFMA, auto S_READ, int rst, int kcopy, int wst) {
+    constexpr int SPAN = (NM * 3) / 4;
+    constexpr int nd = decltype(COPY)::value ? ND : 0;
+    constexpr int nx = nd + NR;
+    constexpr int sm = decltype(S_MFMA)::value, sr = decltype(S_READ)::value;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int fm = i / FN, fn = i % FN;
+      if constexpr (decltype(DO_MFMA)::value)
+        acc[fm][fn] = MM::mma(fb[sm][fn], fa[sm][fm], acc[fm][fn]);
+#pragma unroll
+      for (int x = 0; x < nx; ++x) {
+        if (x * SPAN / nx != i) continue;
+        if (x < 2 * nd) {
+          if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
+          else fread_one(rst, sr, x / 2);
+        } else {
+          fread_one(rst, sr, x - nd);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  (void)sizeof(F);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto wait_all = [&]() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8)); };  // vmcnt(0)
+
+  const int nk = (K + BK - 1) / BK;
+  // prologue: tile 0 in stage 0
+#pragma unroll
+  for (int x = 0; x < ND; ++x) dma_one(0, 0, x);
+  wait_all();
+  __syncthreads();
+  // Trip 0 runs the same body: its "step 1 of the previous tile" MFMAs use
+  // zeroed fragments and add exactly 0.
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) fa[1][fm] = zero_h8();
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    // first half: step 1 of tile kt-1, copies of tile kt+1, step-0 fragments of tile kt
+    half(T{}, T{}, I1{}, I0{}, st, (kt + 1) * BK, st ^ 1);
+    // second half: step 0 of tile kt, step-1 fragments of tile kt
+    half(T{}, F{}, I0{}, I1{}, st, 0, 0);
+    wait_all();
+    __syncthreads();
+  }
+  // the last tile's step 1 (its fragments were read in the last trip)
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+
+  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+        h4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
+        buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                     (_Float16)acc[fm][fn][e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Element-wise instance: any alignment, any leading dimensions (a8).  Same
 // tiling and arithmetic as the tile family, but every global access is a
 // 2-byte access with its own bounds check; it exists for operands outside the
@@ -567,6 +1077,22 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((tile_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g), dim3(64 * WGM * WGN),
                      0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF, int S>
+hipError_t launch_dtile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((dtile_kernel<BM, BN, WGM, WGN, MF, S>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_d2tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((d2tile_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g), dim3(64 * WGM * WGN), 0,
+                     s, a);
   return hipGetLastError();
 }
 

@@ -131,8 +131,10 @@ Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
     if (c.kernel < 0) c.kernel = kGenericKernel;
     return c;
   }
-  static const char* const order[] = {"tile_256x256_w2x2_m32", "tile_256x128_w2x2_m32",
-                                      "tile_128x128_w2x2_m32", "tile_128x64_w2x2_m32",
+  // Largest tile that still gives every CU a workgroup; the measured best
+  // instance of each tile size on MI355X (8192^3 / 4096^3 / LLM shapes).
+  static const char* const order[] = {"d2tile_256x256_w2x4_m16", "dtile_256x128_w2x2_m16_s4",
+                                      "dtile_128x128_w2x2_m16_s4", "tile_128x64_w2x2_m32",
                                       "tile_64x64_w2x2_m32"};
   const int n = (int)(sizeof(order) / sizeof(order[0]));
   for (int t = 0; t < n; ++t) {

@@ -138,9 +138,9 @@ def test_heuristic_picks_by_shape(inspect_handle):
     h = inspect_handle
     names = mh.kernel_names()
     assert names[plan(h, 16, 4096, 4096)[1]].startswith("skinny_")
-    assert names[plan(h, 8192, 8192, 8192)[1]] == "tile_256x256_w2x2_m32"
+    assert names[plan(h, 8192, 8192, 8192)[1]] == "d2tile_256x256_w2x4_m16"
     small = names[plan(h, 256, 256, 256)[1]]
-    assert small.startswith("tile_") and small != "tile_256x256_w2x2_m32"
+    assert "tile_" in small and small != "d2tile_256x256_w2x4_m16"
 
 
 def write_table(path, lines):

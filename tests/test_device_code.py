@@ -23,6 +23,15 @@ def mangled(name):
         kind, bm, bn, wm, wn, mf = m.groups()
         tmpl = f"{len(kind) + 7}{kind}_kernel"
         return f"_ZN4mihg{tmpl}ILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"d2tile_(\d+)x(\d+)_w(\d+)x(\d+)_m16", name)
+    if m:
+        bm, bn, wm, wn = m.groups()
+        return f"_ZN4mihg13d2tile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"(dtile)_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)_(?:la|s)(\d+)", name)
+    if m:
+        kind, bm, bn, wm, wn, mf, x = m.groups()
+        return (f"_ZN4mihg12{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}ELi{x}"
+                "EEEvNS_8GemmArgsE")
     m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)", name)
     if m:
         fm, fn, w, u = m.groups()
