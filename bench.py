@@ -223,10 +223,10 @@ def torch_matmul_context(wl, steps=20):
 def measure(lib, p, steps, warmup, cold, with_torch=False):
     wl = Workload(p, cold)
     a, b, c = wl.sets[0]
-    kernel, gm, xcd = lib.plan(a, b, c)
+    kernel, gm, xcd, sk = lib.plan(a, b, c)
     ms, launch_ms, wall, per = time_steps(lib, wl, steps, warmup)
     rec = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "kernel": kernel, "group_m": gm,
-           "xcd_remap": xcd, "cache": "cold" if cold else "warm", "sets": len(wl.sets),
+           "xcd_remap": xcd, "split_k": sk, "cache": "cold" if cold else "warm", "sets": len(wl.sets),
            "ms_per_step": ms, "us_per_call": round(launch_ms * 1e3, 3),
            "us_per_call_median": round(statistics.median(per) * 1e3, 3),
            "tflops": round(p.flops / (ms * 1e-3) / 1e12, 3), "wall_s": wall,
@@ -293,6 +293,7 @@ def main():
                    "accumulate": "fp32", "inputs": f"{p.kind} a*{p.a_scale:.6g} b*{p.b_scale:.6g} seed {p.seed}",
                    "cache": rec["cache"], "operand_sets": rec["sets"], "kernel": rec["kernel"],
                    "group_m": rec["group_m"], "xcd_remap": rec["xcd_remap"],
+                   "split_k": rec["split_k"],
                    "us_per_call": rec["us_per_call"], "us_per_call_median": rec["us_per_call_median"],
                    "parallelism": "none (1 GPU)"},
         "roofline": rec["roofline"],

@@ -66,10 +66,10 @@ _create_ex = _sig("mi_hgemm_create_ex", ctypes.c_int, ctypes.POINTER(_p), ctypes
 _destroy = _sig("mi_hgemm_destroy", ctypes.c_int, _p)
 _run = _sig("mi_hgemm_run", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
             ctypes.c_int, _p)
-_run_kernel = _sig("mi_hgemm_run_kernel", ctypes.c_int, _p, _i32, _i32, _i32, _i64, _i64, _i64,
-                   _p, _i64, _p, _i64, _p, _i64, ctypes.c_int, _p)
+_run_kernel = _sig("mi_hgemm_run_kernel", ctypes.c_int, _p, _i32, _i32, _i32, _i32, _i64, _i64,
+                   _i64, _p, _i64, _p, _i64, _p, _i64, ctypes.c_int, _p)
 _plan = _sig("mi_hgemm_plan", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
-             ctypes.c_int, _I32P, _I32P, _I32P)
+             ctypes.c_int, _I32P, _I32P, _I32P, _I32P)
 _tune = _sig("mi_hgemm_tune", ctypes.c_int, _p, _i64, _i64, _i64, ctypes.c_int, _p, _u32)
 _status_string = _sig("mi_hgemm_status_string", ctypes.c_char_p, ctypes.c_int)
 _last_hip_error = _sig("mi_hgemm_last_hip_error", ctypes.c_int, _p)
@@ -107,18 +107,18 @@ def mi_hgemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN, 
     return _run(h, M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
 
 
-def mi_hgemm_run_kernel(h, kernel_index, group_m, xcd_remap, M, N, K, A, lda, B, ldb, C, ldc,
-                        layout=MI_HGEMM_LAYOUT_TN, stream=None):
-    return _run_kernel(h, kernel_index, group_m, xcd_remap, M, N, K, A, lda, B, ldb, C, ldc,
-                       layout, stream)
+def mi_hgemm_run_kernel(h, kernel_index, group_m, xcd_remap, split_k, M, N, K, A, lda, B, ldb,
+                        C, ldc, layout=MI_HGEMM_LAYOUT_TN, stream=None):
+    return _run_kernel(h, kernel_index, group_m, xcd_remap, split_k, M, N, K, A, lda, B, ldb, C,
+                       ldc, layout, stream)
 
 
 def mi_hgemm_plan(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN):
-    """-> (status, kernel_index, group_m, xcd_remap)"""
-    k, g, x = ctypes.c_int32(-2), ctypes.c_int32(0), ctypes.c_int32(0)
+    """-> (status, kernel_index, group_m, xcd_remap, split_k)"""
+    k, g, x, s = ctypes.c_int32(-2), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     st = _plan(h, M, N, K, A, lda, B, ldb, C, ldc, layout, ctypes.byref(k), ctypes.byref(g),
-               ctypes.byref(x))
-    return st, k.value, g.value, x.value
+               ctypes.byref(x), ctypes.byref(s))
+    return st, k.value, g.value, x.value, s.value
 
 
 def mi_hgemm_tune(h, M, N, K, layout=MI_HGEMM_LAYOUT_TN, stream=None,
@@ -242,22 +242,23 @@ class Hgemm:
         _check(st, "mi_hgemm_run")
         return out
 
-    def run_kernel(self, kernel, A, Bt, out=None, group_m=1, xcd_remap=0, stream=None):
+    def run_kernel(self, kernel, A, Bt, out=None, group_m=1, xcd_remap=0, split_k=1,
+                   stream=None):
         idx = kernel if isinstance(kernel, int) else kernel_names().index(kernel)
         M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
-        st = mi_hgemm_run_kernel(self.handle, idx, group_m, xcd_remap, M, N, K, A.data_ptr(), lda,
-                                 Bt.data_ptr(), ldb, out.data_ptr(), ldc, MI_HGEMM_LAYOUT_TN,
-                                 _stream_ptr(stream, A.device))
+        st = mi_hgemm_run_kernel(self.handle, idx, group_m, xcd_remap, split_k, M, N, K,
+                                 A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc,
+                                 MI_HGEMM_LAYOUT_TN, _stream_ptr(stream, A.device))
         _check(st, "mi_hgemm_run_kernel")
         return out
 
     def plan(self, A, Bt, out=None):
-        """-> (kernel name or None, group_m, xcd_remap) that ``run`` would use."""
+        """-> (kernel name or None, group_m, xcd_remap, split_k) that ``run`` would use."""
         M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
-        st, k, g, x = mi_hgemm_plan(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb,
-                                    out.data_ptr(), ldc)
+        st, k, g, x, s = mi_hgemm_plan(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(),
+                                       ldb, out.data_ptr(), ldc)
         _check(st, "mi_hgemm_plan")
-        return (mi_hgemm_kernel_name(k) if k >= 0 else None), g, x
+        return (mi_hgemm_kernel_name(k) if k >= 0 else None), g, x, s
 
     def tune(self, M, N, K, flags=MI_HGEMM_TUNE_EXHAUSTIVE, stream=None):
         dev = torch.device("cuda", torch.cuda.current_device())

@@ -78,21 +78,21 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 #if !defined(__HIP_DEVICE_COMPILE__)
 #define TILE_DESC(BM, BN, WGM, WGN, MF)                                                     \
   {"tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, 1, 1, \
-   2 * (BM + BN) * kLdsRow * 2, &launch_tile<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
+   2 * (BM + BN) * kLdsRow * 2, 0, &launch_tile<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
 #define DTILE_DESC(BM, BN, WGM, WGN, MF, S)                                             \
   {"dtile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF "_s" #S, FAMILY_TILE, BM, BN, 32,       \
-   WGM * WGN, MF, 1, 1, 4 * (BM + BN) * kDRow * 2, &launch_dtile<BM, BN, WGM, WGN, MF, S>, \
+   WGM * WGN, MF, 1, 1, 4 * (BM + BN) * kDRow * 2, 1, &launch_dtile<BM, BN, WGM, WGN, MF, S>, \
    &grid_tile<BM, BN>},
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
-   1, 2 * (BM + BN) * kD2Row * 2, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+   1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
 #define SKINNY_DESC(FM, FN, W, U)                                                          \
   {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
-   W * 16 * FM * 16 * FN * 4, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
+   W * 16 * FM * 16 * FN * 4, 0, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
 
 const KernelDesc kKernels[] = {
     // element-wise instance: any alignment, any leading dimensions (must stay first)
-    {"generic_64x64_w2x2_m32", FAMILY_TILE, 64, 64, 64, 4, 32, 0, 1, 128 * 64 * 2,
+    {"generic_64x64_w2x2_m32", FAMILY_TILE, 64, 64, 64, 4, 32, 0, 1, 128 * 64 * 2, 0,
      &launch_generic<64, 64, 2, 2, 32>, &grid_tile<64, 64>},
     MIHG_TILE_INSTANCES(TILE_DESC)
     MIHG_DTILE_INSTANCES(DTILE_DESC)

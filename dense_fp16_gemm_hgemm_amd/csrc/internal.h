@@ -18,7 +18,10 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t group_m;    // tile rows per raster group (>= 1)
   int32_t xcd_remap;  // 1: undo the round-robin workgroup -> XCD dispatch
-  int32_t pad_;
+  int32_t splitk;     // K slices per output tile (1: no split)
+  int32_t kchunk;     // K elements per slice (a multiple of 64) when splitk > 1
+  float* ws;          // split-K partial tiles (splitk > 1)
+  int* cnt;           // split-K arrival counters, one per output tile, zero between launches
 };
 
 enum Family : int32_t {
@@ -36,6 +39,7 @@ struct KernelDesc {
   int32_t aligned;     // 1: requires the 16-byte alignment class
   int32_t unroll;      // skinny: MFMA k-steps per load group
   int32_t lds_bytes;
+  int32_t splitk_ok;   // 1: honours GemmArgs::splitk > 1
   hipError_t (*launch)(const GemmArgs&, hipStream_t);
   int64_t (*grid)(int32_t M, int32_t N);  // workgroups for an M x N output
 };

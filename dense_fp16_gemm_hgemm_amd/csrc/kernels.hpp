@@ -454,12 +454,19 @@ dtile_kernel(GemmArgs p) {
   static_assert(FM % 4 == 0 || MF == 32 || true, "");
 
   __shared__ __attribute__((aligned(1024))) DStages<BM, BN> lds;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int M = p.M, N = p.N, K = p.K;
+  // split-K: workgroup id = tile * splitk + slice; slice s covers K range
+  // [s * kchunk, min(K, (s + 1) * kchunk))
+  const int splitk = p.splitk;
+  const int tile_id = blockIdx.x / splitk, slice = blockIdx.x - tile_id * splitk;
+  const int k_begin = splitk > 1 ? slice * p.kchunk : 0;
+  const int k_len = splitk > 1 ? min(p.kchunk, K - k_begin) : K;
   int tm, tn;
-  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  tile_coords(tile_id, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
   // DMA: lane -> (row l/4 of a 16-row block, logical chunk (l%4)^(l/16)).
@@ -564,11 +571,11 @@ dtile_kernel(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   };
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (k_len + BK - 1) / BK;
   // prologue: tiles 0 .. S-2 in flight; tiles 0 and 1 published
-  dma(dstage<0>(lds), 0);
-  dma(dstage<1>(lds), BK);
-  if constexpr (S == 4) dma(dstage<2>(lds), 2 * BK);
+  dma(dstage<0>(lds), k_begin);
+  dma(dstage<1>(lds), k_begin + BK);
+  if constexpr (S == 4) dma(dstage<2>(lds), k_begin + 2 * BK);
   wait_dma();
   __syncthreads();
   fread(dstage<0>(lds), 0);
@@ -590,7 +597,7 @@ dtile_kernel(GemmArgs p) {
     constexpr int SPAN = (NM * 3) / 4;
     _Float16* wst = dstage<SW>(lds);
     const _Float16* rst = dstage<SN>(lds);
-    const int kw = (kt + S - 1) * BK;
+    const int kw = k_begin + (kt + S - 1) * BK;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int s = i / (FM * FN), fm = (i / FN) % FM, fn = i % FN;
@@ -625,6 +632,59 @@ dtile_kernel(GemmArgs p) {
   }
   // drain the DMA still in flight before the workgroup exits
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
+
+  if (splitk > 1) {
+    // Split-K fix-up.  Every slice stores its fp32 partial tile in lane order
+    // (one contiguous 1 KiB per wave and store), publishes it with a
+    // device-scope release and counts itself in; the slice that arrives last
+    // sums all partials in slice order 0..splitk-1 -- the same order whoever
+    // arrives last, so the result does not depend on timing -- writes C and
+    // resets the counter for the next launch.
+    constexpr int NV = FM * FN * (MM::NACC / 4);  // float4 values per lane
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    f4* wsl = reinterpret_cast<f4*>(p.ws) + ((int64_t)tile_id * splitk + slice) * (NV * NT);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int v = (fm * FN + fn) * (MM::NACC / 4) + g;
+          f4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
+          wsl[v * NT + tid] = x;
+        }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&p.cnt[tile_id], 1) == splitk - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const f4* wst0 = reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int v = (fm * FN + fn) * (MM::NACC / 4) + g;
+          f4 s4 = {0.f, 0.f, 0.f, 0.f};
+          for (int s2 = 0; s2 < splitk; ++s2) {
+            f4 x;
+            if (s2 == slice) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
+            } else {
+              x = __builtin_nontemporal_load(&wst0[(int64_t)s2 * (NV * NT) + v * NT + tid]);
+            }
+            s4 += x;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[fm][fn][4 * g + e] = s4[e];
+        }
+    if (tid == 0) p.cnt[tile_id] = 0;
+  }
 
   _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
@@ -1082,7 +1142,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN, int MF, int S>
 hipError_t launch_dtile(const GemmArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
   hipLaunchKernelGGL((dtile_kernel<BM, BN, WGM, WGN, MF, S>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();

@@ -47,8 +47,13 @@ struct Config {
   int32_t kernel = kGenericKernel;
   int32_t group_m = 1;
   int32_t xcd = 0;
-  double us = 0.0;  // measured time when tuned; 0 for heuristic picks
+  int32_t splitk = 1;  // K slices per output tile (instances with splitk_ok only)
+  double us = 0.0;     // measured time when tuned; 0 for heuristic picks
 };
+
+// Split-K workspace the handle owns: fp32 partial tiles and per-tile counters.
+constexpr size_t kWsBytes = size_t(64) << 20;
+constexpr int kMaxTiles = 1 << 16;
 
 struct Key {
   int64_t M, N, K;
@@ -63,6 +68,8 @@ struct Key {
 struct mi_hgemm_ctx {
   int device = -1;
   bool no_device = false;
+  float* ws = nullptr;  // kWsBytes of split-K partials
+  int* cnt = nullptr;   // kMaxTiles split-K counters, zero between launches
   int last_hip_error = 0;
   std::string table_path;  // resolved path (may be empty)
   std::map<Key, Config> table;
@@ -145,6 +152,23 @@ Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
   }
   c.group_m = 8;
   c.xcd = 1;
+  // Too few output tiles to fill 256 CUs and a long K: split K over 128x128
+  // tiles (the fix-up reads back (splitk - 1) fp32 partial tiles per tile).
+  const int sk = find_kernel("dtile_128x128_w2x2_m16_s4");
+  if (sk >= 0 && K >= 1024 && kKernels[sk].grid((int32_t)M, (int32_t)N) < 192) {
+    {
+      const int64_t tiles = kKernels[sk].grid((int32_t)M, (int32_t)N);
+      int s = 1;
+      while (s < 8 && tiles * s * 2 <= 384 && K / (s * 2) >= 512) s *= 2;
+      if (s > 1 && tiles <= kMaxTiles &&
+          (size_t)tiles * s * 128 * 128 * sizeof(float) <= kWsBytes) {
+        c.kernel = sk;
+        c.splitk = s;
+        c.group_m = 1;
+        c.xcd = 0;
+      }
+    }
+  }
   return c;
 }
 
@@ -170,7 +194,7 @@ Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
 }
 
 // Table file: one entry per line,
-//   <arch> <M> <N> <K> <layout> <a16|any> <kernel name> <group_m> <xcd_remap> <microseconds>
+//   <arch> <M> <N> <K> <layout> <a16|any> <kernel name> <group_m> <xcd_remap> <microseconds> [<split_k>]
 // '#' starts a comment.  Lines for another arch or layout are skipped; lines
 // that do not parse, or name an unknown kernel, mark the table as damaged.
 bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
@@ -188,18 +212,20 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
     if (*p == '#' || *p == '\n' || *p == '\r' || *p == '\0') continue;
     char arch[64], layout[16], align[16], kname[128];
     long long M, N, K;
-    int gm, xcd;
+    int gm, xcd, sk = 1;
     double us;
-    const int got = std::sscanf(p, "%63s %lld %lld %lld %15s %15s %127s %d %d %lf", arch, &M, &N,
-                                &K, layout, align, kname, &gm, &xcd, &us);
-    if (got != 10 || M < 1 || N < 1 || K < 1 || gm < 1 || (xcd != 0 && xcd != 1)) {
+    const int got = std::sscanf(p, "%63s %lld %lld %lld %15s %15s %127s %d %d %lf %d", arch, &M,
+                                &N, &K, layout, align, kname, &gm, &xcd, &us, &sk);
+    if ((got != 10 && got != 11) || M < 1 || N < 1 || K < 1 || gm < 1 || (xcd != 0 && xcd != 1) ||
+        sk < 1 || sk > 64) {
       clean = false;
       continue;
     }
     if (std::strcmp(arch, kArch) != 0 || std::strcmp(layout, "TN") != 0) continue;
     const int k = find_kernel(kname);
     const bool al = std::strcmp(align, "a16") == 0;
-    if (k < 0 || (!al && std::strcmp(align, "any") != 0) || (!al && kKernels[k].aligned)) {
+    if (k < 0 || (!al && std::strcmp(align, "any") != 0) || (!al && kKernels[k].aligned) ||
+        (sk > 1 && !kKernels[k].splitk_ok)) {
       clean = false;
       continue;
     }
@@ -207,6 +233,7 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
     c.kernel = k;
     c.group_m = gm;
     c.xcd = xcd;
+    c.splitk = sk;
     c.us = us;
     h->table[Key{M, N, K, al ? 1 : 0}] = c;
   }
@@ -215,9 +242,9 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
 }
 
 bool write_entry(FILE* f, const Key& k, const Config& c) {
-  return std::fprintf(f, "%s %lld %lld %lld TN %s %s %d %d %.3f\n", kArch, (long long)k.M,
+  return std::fprintf(f, "%s %lld %lld %lld TN %s %s %d %d %.3f %d\n", kArch, (long long)k.M,
                       (long long)k.N, (long long)k.K, k.aligned ? "a16" : "any",
-                      kKernels[c.kernel].name, c.group_m, c.xcd, c.us) > 0;
+                      kKernels[c.kernel].name, c.group_m, c.xcd, c.us, c.splitk) > 0;
 }
 
 std::string default_table_path() {
@@ -273,7 +300,24 @@ mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N,
   a.K = (int32_t)K;
   a.group_m = std::max(1, c.group_m);
   a.xcd_remap = c.xcd ? 1 : 0;
-  a.pad_ = 0;
+  a.splitk = 1;
+  a.kchunk = (int32_t)K;
+  a.ws = h->ws;
+  a.cnt = h->cnt;
+  if (c.splitk > 1) {
+    if (!kd.splitk_ok || !h->ws || !h->cnt) return MI_HGEMM_ERR_UNSUPPORTED;
+    // slices of a multiple of 64 K elements; empty trailing slices are dropped
+    const int64_t chunk = ((K + c.splitk - 1) / c.splitk + 63) / 64 * 64;
+    const int64_t sk = (K + chunk - 1) / chunk;
+    const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
+    if (sk > 1) {
+      if (tiles > kMaxTiles || tiles * sk > INT32_MAX ||
+          (size_t)tiles * sk * kd.bm * kd.bn * sizeof(float) > kWsBytes)
+        return MI_HGEMM_ERR_UNSUPPORTED;
+      a.splitk = (int32_t)sk;
+      a.kchunk = (int32_t)chunk;
+    }
+  }
   const hipError_t e = kd.launch(a, stream);
   if (e != hipSuccess) return hip_fail(h, e);
   return MI_HGEMM_OK;
@@ -332,6 +376,18 @@ mi_hgemm_status_t mi_hgemm_create_ex(mi_hgemm_handle_t* out, const char* table_p
       delete h;
       return MI_HGEMM_ERR_NO_DEVICE;
     }
+    // split-K workspace: allocated once here, never per call
+    void* ws = nullptr;
+    void* cnt = nullptr;
+    if (hipMalloc(&ws, kWsBytes) == hipSuccess && hipMalloc(&cnt, kMaxTiles * sizeof(int)) == hipSuccess &&
+        hipMemset(cnt, 0, kMaxTiles * sizeof(int)) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
+      h->ws = static_cast<float*>(ws);
+      h->cnt = static_cast<int*>(cnt);
+    } else {
+      if (ws) (void)hipFree(ws);
+      if (cnt) (void)hipFree(cnt);
+      (void)hipGetLastError();
+    }
   }
   bool named = false;
   if (table_path && *table_path) {
@@ -358,6 +414,12 @@ mi_hgemm_status_t mi_hgemm_create(mi_hgemm_handle_t* out, const char* table_path
 }
 
 mi_hgemm_status_t mi_hgemm_destroy(mi_hgemm_handle_t h) {
+  if (!h) return MI_HGEMM_OK;
+  if (h->ws || h->cnt) {
+    DeviceGuard g(h->device);
+    if (h->ws) (void)hipFree(h->ws);
+    if (h->cnt) (void)hipFree(h->cnt);
+  }
   delete h;
   return MI_HGEMM_OK;
 }
@@ -377,7 +439,8 @@ const char* mi_hgemm_kernel_name(int index) {
 mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                 const void* A, int64_t lda, const void* B, int64_t ldb,
                                 const void* C, int64_t ldc, mi_hgemm_layout_t layout,
-                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap) {
+                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
+                                int32_t* split_k) {
   if (!h) return MI_HGEMM_ERR_INVALID_ARG;
   const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
   if (st != MI_HGEMM_OK) return st;
@@ -387,6 +450,7 @@ mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64
   if (kernel_index) *kernel_index = c.kernel;
   if (group_m) *group_m = c.group_m;
   if (xcd_remap) *xcd_remap = c.xcd;
+  if (split_k) *split_k = c.kernel >= 0 ? c.splitk : 1;
   return MI_HGEMM_OK;
 }
 
@@ -403,13 +467,16 @@ mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_
 }
 
 mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index, int32_t group_m,
-                                      int32_t xcd_remap, int64_t M, int64_t N, int64_t K,
+                                      int32_t xcd_remap, int32_t split_k, int64_t M, int64_t N,
+                                      int64_t K,
                                       const void* A, int64_t lda, const void* B, int64_t ldb,
                                       void* C, int64_t ldc, mi_hgemm_layout_t layout,
                                       void* stream) {
   if (!h) return MI_HGEMM_ERR_INVALID_ARG;
   if (kernel_index < 0 || kernel_index >= kNumKernels) return MI_HGEMM_ERR_UNSUPPORTED;
-  if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1)) return MI_HGEMM_ERR_INVALID_ARG;
+  if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1) || split_k < 1 || split_k > 64)
+    return MI_HGEMM_ERR_INVALID_ARG;
+  if (split_k > 1 && !kKernels[kernel_index].splitk_ok) return MI_HGEMM_ERR_UNSUPPORTED;
   const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
   if (st != MI_HGEMM_OK) return st;
   if (kKernels[kernel_index].aligned && !aligned_class(K, A, lda, B, ldb, C, ldc))
@@ -418,6 +485,7 @@ mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
   c.kernel = kernel_index;
   c.group_m = group_m;
   c.xcd = xcd_remap;
+  c.splitk = split_k;
   return run_config(h, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
@@ -515,6 +583,19 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
         c.xcd = r[1];
         cands.push_back(c);
       }
+      // split K when the output tiles alone leave CUs idle
+      const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
+      if (kd.splitk_ok && h->ws && tiles < 256) {
+        for (int s = 2; s <= 16; s *= 2) {
+          if (K / s < 256 || tiles * s > 1024 ||
+              (size_t)tiles * s * kd.bm * kd.bn * sizeof(float) > kWsBytes)
+            break;
+          Config c;
+          c.kernel = k;
+          c.splitk = s;
+          cands.push_back(c);
+        }
+      }
     } else {
       if (heuristic_only && M > 128) continue;
       Config c;
@@ -523,7 +604,8 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     }
   }
   if (std::find_if(cands.begin(), cands.end(), [&](const Config& c) {
-        return c.kernel == start.kernel && c.group_m == start.group_m && c.xcd == start.xcd;
+        return c.kernel == start.kernel && c.group_m == start.group_m && c.xcd == start.xcd &&
+               c.splitk == start.splitk;
       }) == cands.end())
     cands.push_back(start);
 

@@ -28,7 +28,15 @@
  *   - Nothing is allocated per call by mi_hgemm_run.  No exception crosses the
  *     ABI; every failure is a status code.
  *   - A handle may be shared by threads calling mi_hgemm_run / mi_hgemm_plan
- *     concurrently.  mi_hgemm_tune and mi_hgemm_destroy need exclusive use.
+ *     concurrently, provided their launches are ordered on one stream: a
+ *     handle owns one split-K workspace (below), so launches of one handle
+ *     that may run at the same time on different streams must use separate
+ *     handles.  mi_hgemm_tune and mi_hgemm_destroy need exclusive use.
+ *   - Split-K: a handle created on a device allocates, once, a 64 MiB device
+ *     workspace for fp32 partial tiles and a table of per-tile counters.  For
+ *     shapes whose output tiles alone cannot occupy the device, the dispatcher
+ *     may split K into slices; the last slice to finish sums the partial
+ *     tiles in slice order (deterministic) and writes C.
  */
 #ifndef MI_HGEMM_H
 #define MI_HGEMM_H
@@ -131,23 +139,27 @@ const char* mi_hgemm_kernel_name(int index);
 /*
  * What mi_hgemm_run would launch for these arguments, without launching:
  * validates exactly as mi_hgemm_run and writes the instance index, raster
- * group height and XCD remap flag (any output pointer may be NULL).
- * *kernel_index is -1 when no kernel would run (empty C, or K == 0).
+ * group height, XCD remap flag and requested K split (any output pointer may
+ * be NULL).  *kernel_index is -1 when no kernel would run (empty C, K == 0).
  * Works on inspection handles; device pointers are only compared, never read.
  */
 mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                 const void* A, int64_t lda, const void* B, int64_t ldb,
                                 const void* C, int64_t ldc, mi_hgemm_layout_t layout,
-                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap);
+                                int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
+                                int32_t* split_k);
 
 /*
- * mi_hgemm_run with a forced instance and raster setting (tests, benchmarks,
- * external tuners).  Validation as mi_hgemm_run, plus UNSUPPORTED when the
- * instance needs the 16-byte class and the operands are not in it, or
- * kernel_index is out of range.  group_m >= 1; xcd_remap 0 or 1.
+ * mi_hgemm_run with a forced instance, raster setting and K split (tests,
+ * benchmarks, external tuners).  Validation as mi_hgemm_run, plus
+ * UNSUPPORTED when the instance needs the 16-byte class and the operands are
+ * not in it, kernel_index is out of range, split_k > 1 is asked of an
+ * instance without split-K, or the partial tiles exceed the workspace.
+ * group_m >= 1; xcd_remap 0 or 1; 1 <= split_k <= 64 (the effective split may
+ * be smaller: slices are whole multiples of 64 in K).
  */
 mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
-                                      int32_t group_m, int32_t xcd_remap,
+                                      int32_t group_m, int32_t xcd_remap, int32_t split_k,
                                       int64_t M, int64_t N, int64_t K,
                                       const void* A, int64_t lda, const void* B, int64_t ldb,
                                       void* C, int64_t ldc, mi_hgemm_layout_t layout,

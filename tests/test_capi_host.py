@@ -100,7 +100,7 @@ def test_validation_status_codes(inspect_handle):
 
 def test_empty_and_k_zero_launch_nothing(inspect_handle):
     h = inspect_handle
-    assert plan(h, 0, 64, 64, A=0, B=0, C=0) == (mh.MI_HGEMM_OK, -1, 1, 0)
+    assert plan(h, 0, 64, 64, A=0, B=0, C=0) == (mh.MI_HGEMM_OK, -1, 1, 0, 1)
     assert plan(h, 64, 0, 64, A=0, B=0, C=0, ldc=1)[:2] == (mh.MI_HGEMM_OK, -1)
     assert plan(h, 64, 0, 64, A=0, B=0, C=0, ldc=0)[0] == mh.MI_HGEMM_ERR_INVALID_ARG
     assert plan(h, 64, 64, 0, lda=1, ldb=1, A=0, B=0)[:2] == (mh.MI_HGEMM_OK, -1)  # K == 0: fill only
@@ -112,12 +112,16 @@ def test_inspection_handle_does_not_launch(inspect_handle):
     assert st == mh.MI_HGEMM_ERR_NO_DEVICE
     assert mh.mi_hgemm_run(h, 0, 64, 64, 0, 64, 0, 64, 0, 64) == mh.MI_HGEMM_OK
     assert mh.mi_hgemm_tune(h, 64, 64, 64) == mh.MI_HGEMM_ERR_NO_DEVICE
-    assert mh.mi_hgemm_run_kernel(h, 0, 1, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+    assert mh.mi_hgemm_run_kernel(h, 0, 1, 0, 1, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
         mh.MI_HGEMM_ERR_NO_DEVICE
-    assert mh.mi_hgemm_run_kernel(h, 999, 1, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+    assert mh.mi_hgemm_run_kernel(h, 999, 1, 0, 1, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
         mh.MI_HGEMM_ERR_UNSUPPORTED
-    assert mh.mi_hgemm_run_kernel(h, 0, 0, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+    assert mh.mi_hgemm_run_kernel(h, 0, 0, 0, 1, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
         mh.MI_HGEMM_ERR_INVALID_ARG
+    assert mh.mi_hgemm_run_kernel(h, 0, 1, 0, 0, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_INVALID_ARG
+    assert mh.mi_hgemm_run_kernel(h, 0, 1, 0, 2, 64, 64, 64, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_UNSUPPORTED   # the element-wise instance has no split-K
 
 
 def test_misalignment_selects_the_elementwise_instance(inspect_handle):
@@ -130,7 +134,7 @@ def test_misalignment_selects_the_elementwise_instance(inspect_handle):
     assert plan(h, 256, 256, 256, lda=260)[1] == generic       # lda not a multiple of 8
     assert plan(h, 256, 256, 256, ldb=264)[1] != generic       # padded but aligned
     assert plan(h, 256, 256, 256, ldb=(1 << 21) + 8)[1] == generic  # beyond 32-bit tile offsets
-    aligned_only = mh.mi_hgemm_run_kernel(h, 1, 1, 0, 256, 256, 250, A0, 256, B0, 256, C0, 256)
+    aligned_only = mh.mi_hgemm_run_kernel(h, 1, 1, 0, 1, 256, 256, 250, A0, 256, B0, 256, C0, 256)
     assert aligned_only == mh.MI_HGEMM_ERR_UNSUPPORTED
 
 
@@ -141,6 +145,21 @@ def test_heuristic_picks_by_shape(inspect_handle):
     assert names[plan(h, 8192, 8192, 8192)[1]] == "d2tile_256x256_w2x4_m16"
     small = names[plan(h, 256, 256, 256)[1]]
     assert "tile_" in small and small != "d2tile_256x256_w2x4_m16"
+    r = plan(h, 256, 4096, 4096)                     # 16 large tiles: split K over 128x128 tiles
+    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] > 1
+
+
+def test_table_split_k_column(tmp_path, monkeypatch):
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    names = mh.kernel_names()
+    p = tmp_path / "sk.tsv"
+    write_table(p, ["gfx950 256 4096 4096 TN a16 dtile_128x128_w2x2_m16_s4 1 0 9.0 4",
+                    "gfx950 128 128 128 TN a16 tile_64x64_w2x2_m16 1 0 1.0 4"])  # no split-K
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_WARN_TABLE_DEFAULTS and mh.mi_hgemm_table_size(h) == 1
+    r = plan(h, 256, 4096, 4096)
+    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 4
+    mh.mi_hgemm_destroy(h)
 
 
 def write_table(path, lines):
@@ -162,13 +181,13 @@ def test_table_exact_and_nearest_shape(tmp_path, monkeypatch):
     try:
         assert mh.mi_hgemm_table_size(h) == 2
         r = plan(h, 1000, 2000, 3000)
-        assert names[r[1]] == "tile_64x64_w2x2_m16" and r[2:] == (4, 1)
+        assert names[r[1]] == "tile_64x64_w2x2_m16" and r[2:] == (4, 1, 1)
         r = plan(h, 1000, 2000, 3000 * 2)                  # one factor of 2 away: nearest entry
         assert names[r[1]] == "tile_64x64_w2x2_m16"
         r = plan(h, 1000 * 4, 2000, 3000)                  # too far: heuristics
         assert names[r[1]] != "tile_64x64_w2x2_m16"
         r = plan(h, 512, 512, 512, lda=516)                # unaligned class entry
-        assert r[1:] == (0, 2, 0)
+        assert r[1:] == (0, 2, 0, 1)
         out = tmp_path / "saved.tsv"
         assert mh.mi_hgemm_table_save(h, str(out)) == mh.MI_HGEMM_OK
         st2, h2 = mh.mi_hgemm_create_ex(str(out), mh.MI_HGEMM_CREATE_NO_DEVICE)

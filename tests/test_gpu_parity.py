@@ -278,10 +278,46 @@ def test_tuner_builds_a_table_entry(tmp_path):
     assert len(lines) == 1 and lines[0].startswith("gfx950 192 640 320 TN a16 ")
     A, Bt = rand_problem(192, 640, 320, "randn", seed=4)
     dA, dB = gpu(A), gpu(Bt)
-    name, _, _ = h.plan(dA, dB)
+    name, _, _, _ = h.plan(dA, dB)
     assert name == lines[0].split()[6]
     check_tolerance(host(h.run(dA, dB)), oracle.hgemm_tn(A, Bt), "tuned")
     h2 = mh.Hgemm(str(table))
     assert h2.create_status == mh.MI_HGEMM_OK and h2.table_size() == 1
     h.close()
     h2.close()
+
+
+SPLIT_CASES = [(256, 512, 4096, 2), (256, 512, 4096, 4), (200, 300, 2560, 3), (128, 256, 1000, 4),
+               (64, 128, 8192, 8), (256, 4096, 4096, 4)]
+
+
+@pytest.mark.parametrize("M,N,K,sk", SPLIT_CASES, ids=lambda v: str(v))
+def test_split_k_integer_bitexact(lib, M, N, K, sk):
+    """Split-K sums fp32 partial tiles; on integer inputs every partial and
+    total is exact, so the result must equal the oracle bit for bit."""
+    A, Bt = rand_problem(M, N, K, "int", seed=M + N + K + sk)
+    log(f"split-K {M}x{N}x{K} s={sk}")
+    got = host(lib.run_kernel("dtile_128x128_w2x2_m16_s4", gpu(A), gpu(Bt), padded_out(M, N),
+                              split_k=sk))
+    if M * N * K <= 256 * 512 * 4096:
+        check_bitexact(got, oracle.hgemm_tn(A, Bt), f"split {sk}")
+    else:
+        r, c = sample_indices(M, N, 4096, seed=sk)
+        check_bitexact(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), f"split {sk}")
+
+
+def test_split_k_dispatch_randn_deterministic(lib):
+    """The dispatcher splits K for 256x4096x4096; results are within tolerance,
+    identical over repeated launches (fixed summation order, counters reset)."""
+    p = inputs.llm()[8]          # M = 256, (N, K) = (4096, 4096)
+    assert (p.M, p.N, p.K) == (256, 4096, 4096)
+    A, Bt = inputs.make(p)
+    dA, dB = gpu(A), gpu(Bt)
+    name, _, _, sk = lib.plan(dA, dB)
+    log(f"dispatch {p.name}: {name} split {sk}")
+    assert sk > 1
+    first = host(lib.run(dA, dB))
+    for _ in range(3):
+        assert np.array_equal(host(lib.run(dA, dB)).view(np.uint16), first.view(np.uint16))
+    r, c = sample_indices(p.M, p.N, 4096, seed=1)
+    check_tolerance(first[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
