@@ -81,7 +81,8 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
    2 * (BM + BN) * kLdsRow * 2, 0, &launch_tile<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
 #define DTILE_DESC(BM, BN, WGM, WGN, MF, S)                                             \
   {"dtile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF "_s" #S, FAMILY_TILE, BM, BN, 32,       \
-   WGM * WGN, MF, 1, 1, 4 * (BM + BN) * kDRow * 2, 1, &launch_dtile<BM, BN, WGM, WGN, MF, S>, \
+   WGM * WGN, MF, 1, 1, 4 * (BM + BN) * kDRow * 2, dtile_splits<BM, BN>() ? 1 : 0,          \
+   &launch_dtile<BM, BN, WGM, WGN, MF, S>,                                                   \
    &grid_tile<BM, BN>},
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \

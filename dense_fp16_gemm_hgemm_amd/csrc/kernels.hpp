@@ -118,6 +118,10 @@ __device__ inline int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3
 // host only sends operands here whose tile rows span less than 2^31 bytes.
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw buffer, 32-bit data format
+// Cache-policy operand of the buffer builtins: bit 4 is SC1, which on the
+// gfx94x/gfx950 memory model gives an access device scope (coherent across
+// the XCDs' L2 caches) without any cache-wide write-back or invalidate.
+constexpr int kDeviceScope = 16;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -436,6 +440,12 @@ __device__ __forceinline__ void dtrip_schedule() {
   }
 }
 
+// Split-K is compiled into the direct-to-LDS instances of at most 256 x 128
+// outputs: split-K pays only when output tiles are few, which larger tiles
+// make worse, and the fix-up's registers would spill in the 256 x 256 ones.
+template <int BM, int BN>
+constexpr bool dtile_splits() { return BM * BN <= 256 * 128; }
+
 template <int BM, int BN, int WGM, int WGN, int MF, int S>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 dtile_kernel(GemmArgs p) {
@@ -461,7 +471,7 @@ dtile_kernel(GemmArgs p) {
   const int M = p.M, N = p.N, K = p.K;
   // split-K: workgroup id = tile * splitk + slice; slice s covers K range
   // [s * kchunk, min(K, (s + 1) * kchunk))
-  const int splitk = p.splitk;
+  const int splitk = dtile_splits<BM, BN>() ? p.splitk : 1;
   const int tile_id = blockIdx.x / splitk, slice = blockIdx.x - tile_id * splitk;
   const int k_begin = splitk > 1 ? slice * p.kchunk : 0;
   const int k_len = splitk > 1 ? min(p.kchunk, K - k_begin) : K;
@@ -633,16 +643,27 @@ dtile_kernel(GemmArgs p) {
   // drain the DMA still in flight before the workgroup exits
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
 
-  if (splitk > 1) {
+  if (dtile_splits<BM, BN>() && splitk > 1) {
     // Split-K fix-up.  Every slice stores its fp32 partial tile in lane order
-    // (one contiguous 1 KiB per wave and store), publishes it with a
-    // device-scope release and counts itself in; the slice that arrives last
-    // sums all partials in slice order 0..splitk-1 -- the same order whoever
-    // arrives last, so the result does not depend on timing -- writes C and
-    // resets the counter for the next launch.
+    // (one contiguous 1 KiB per wave and store) and counts itself in; the
+    // slice that arrives last sums all partials in slice order 0..splitk-1 --
+    // the same order whoever arrives last, so the result does not depend on
+    // timing -- writes C and resets the counter for the next launch.
+    //
+    // The workgroups of one tile run on different XCDs, whose L2 caches are
+    // not coherent with each other.  A device-scope fence would make that
+    // safe by writing back and invalidating the whole L2 of the XCD, once per
+    // workgroup, which costs the other workgroups their cached operand lines.
+    // Instead only the workspace traffic is made device-coherent: partials
+    // are stored and loaded with device scope (cache policy SC1, which writes
+    // through and reads past the XCD's L2), every wave waits until its stores
+    // are acknowledged before the workgroup counts itself in, and the
+    // counter is a device-scope atomic.  The last slice reads the partials
+    // only after its atomic has returned.
     constexpr int NV = FM * FN * (MM::NACC / 4);  // float4 values per lane
     typedef float f4 __attribute__((ext_vector_type(4)));
-    f4* wsl = reinterpret_cast<f4*>(p.ws) + ((int64_t)tile_id * splitk + slice) * (NV * NT);
+    const auto rsw = make_rsrc(reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT),
+                               (uint32_t)(splitk * NV * NT * 16));
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -653,37 +674,54 @@ dtile_kernel(GemmArgs p) {
           f4 x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
-          wsl[v * NT + tid] = x;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsw,
+                                                 (uint32_t)(((slice * NV + v) * NT + tid) * 16), 0,
+                                                 kDeviceScope);
         }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));  // vmcnt(0): partial stores acknowledged
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&p.cnt[tile_id], 1) == splitk - 1;
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&p.cnt[tile_id], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == splitk - 1;
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    const f4* wst0 = reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT);
+    // running sum over slices 0..splitk-1 in order, VG float4 values per lane
+    // at a time; a slice's VG loads are issued together before any is added
+    constexpr int VG = NV < 16 ? NV : 16;
+    static_assert(NV % VG == 0, "whole groups");
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int v0 = 0; v0 < NV; v0 += VG) {
+      f4 sum[VG];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
+      for (int u = 0; u < VG; ++u) sum[u] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < splitk; ++s2) {
+        if (s2 == slice) {
 #pragma unroll
-        for (int g = 0; g < MM::NACC / 4; ++g) {
-          const int v = (fm * FN + fn) * (MM::NACC / 4) + g;
-          f4 s4 = {0.f, 0.f, 0.f, 0.f};
-          for (int s2 = 0; s2 < splitk; ++s2) {
-            f4 x;
-            if (s2 == slice) {
+          for (int u = 0; u < VG; ++u) {
+            const int v = v0 + u, fg = v / (MM::NACC / 4), g = v % (MM::NACC / 4);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
-            } else {
-              x = __builtin_nontemporal_load(&wst0[(int64_t)s2 * (NV * NT) + v * NT + tid]);
-            }
-            s4 += x;
+            for (int e = 0; e < 4; ++e) sum[u][e] += acc[fg / FN][fg % FN][4 * g + e];
           }
+        } else {
+          f4 x[VG];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[fm][fn][4 * g + e] = s4[e];
+          for (int u = 0; u < VG; ++u)
+            x[u] = __builtin_bit_cast(
+                f4, __builtin_amdgcn_raw_buffer_load_b128(
+                        rsw, (uint32_t)(((s2 * NV + v0 + u) * NT + tid) * 16), 0, kDeviceScope));
+#pragma unroll
+          for (int u = 0; u < VG; ++u) sum[u] += x[u];
         }
-    if (tid == 0) p.cnt[tile_id] = 0;
+      }
+#pragma unroll
+      for (int u = 0; u < VG; ++u) {
+        const int v = v0 + u, fg = v / (MM::NACC / 4), g = v % (MM::NACC / 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[fg / FN][fg % FN][4 * g + e] = sum[u][e];
+      }
+    }
+    if (tid == 0)
+      __hip_atomic_store(&p.cnt[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
@@ -1142,7 +1180,8 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 template <int BM, int BN, int WGM, int WGN, int MF, int S>
 hipError_t launch_dtile(const GemmArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  const int sk = dtile_splits<BM, BN>() ? a.splitk : 1;
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * sk;
   hipLaunchKernelGGL((dtile_kernel<BM, BN, WGM, WGN, MF, S>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();

@@ -289,21 +289,39 @@ def test_tuner_builds_a_table_entry(tmp_path):
 
 SPLIT_CASES = [(256, 512, 4096, 2), (256, 512, 4096, 4), (200, 300, 2560, 3), (128, 256, 1000, 4),
                (64, 128, 8192, 8), (256, 4096, 4096, 4)]
+SPLIT_KERNELS = ["dtile_128x128_w2x2_m16_s4", "dtile_256x128_w2x2_m16_s4",
+                 "dtile_128x256_w2x2_m16_s4"]
 
 
+@pytest.mark.parametrize("kernel", SPLIT_KERNELS)
 @pytest.mark.parametrize("M,N,K,sk", SPLIT_CASES, ids=lambda v: str(v))
-def test_split_k_integer_bitexact(lib, M, N, K, sk):
+def test_split_k_integer_bitexact(lib, kernel, M, N, K, sk):
     """Split-K sums fp32 partial tiles; on integer inputs every partial and
     total is exact, so the result must equal the oracle bit for bit."""
     A, Bt = rand_problem(M, N, K, "int", seed=M + N + K + sk)
-    log(f"split-K {M}x{N}x{K} s={sk}")
-    got = host(lib.run_kernel("dtile_128x128_w2x2_m16_s4", gpu(A), gpu(Bt), padded_out(M, N),
-                              split_k=sk))
+    log(f"split-K {kernel} {M}x{N}x{K} s={sk}")
+    got = host(lib.run_kernel(kernel, gpu(A), gpu(Bt), padded_out(M, N), split_k=sk))
     if M * N * K <= 256 * 512 * 4096:
         check_bitexact(got, oracle.hgemm_tn(A, Bt), f"split {sk}")
     else:
         r, c = sample_indices(M, N, 4096, seed=sk)
         check_bitexact(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), f"split {sk}")
+
+
+@pytest.mark.parametrize("kernel", SPLIT_KERNELS)
+def test_split_k_back_to_back_fresh_partials(lib, kernel):
+    """Consecutive launches of one geometry reuse the same workspace slots and
+    counters.  With different inputs each launch must read the partials of
+    its own slices, not those the previous launch left behind."""
+    M, N, K, sk = 256, 1024, 4096, 4
+    probs = [rand_problem(M, N, K, "int", seed=s) for s in (11, 12, 13)]
+    outs = [padded_out(M, N) for _ in probs]
+    dev = [(gpu(A), gpu(Bt)) for A, Bt in probs]
+    log(f"split-K back-to-back {kernel} {M}x{N}x{K} s={sk}")
+    for (dA, dB), out in zip(dev, outs):   # no synchronisation in between
+        lib.run_kernel(kernel, dA, dB, out, split_k=sk)
+    for i, ((A, Bt), out) in enumerate(zip(probs, outs)):
+        check_bitexact(host(out), oracle.hgemm_tn(A, Bt), f"launch {i}")
 
 
 def test_split_k_dispatch_randn_deterministic(lib):
