@@ -24,8 +24,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+# The kernels index their accumulator and fragment arrays with loop counters
+# that must become constants: every such loop is marked for full unrolling,
+# and the threshold is raised so that the largest (64 MFMAs per half trip)
+# are unrolled too instead of leaving the arrays in scratch memory.
 DEVICE = ["--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-pragma-unroll-threshold=1000000",
           "-Wno-unused-command-line-argument"]
 
 

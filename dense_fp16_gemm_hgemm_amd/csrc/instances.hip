@@ -45,6 +45,7 @@ namespace mihg {
 
 #define MIHG_D2TILE_INSTANCES(X) \
   X(256, 256, 2, 4)               \
+  X(256, 256, 2, 2)               \
   X(256, 128, 2, 2)               \
   X(128, 128, 2, 2)
 
