@@ -185,10 +185,14 @@ def cpu_baseline(p, A, Bt, gpu_c, target_s):
         vals = orc.hgemm_tn_entries(A, Bt, r, c)
         return time.perf_counter() - t0, vals.reshape(R, p.N)
 
-    R0 = max(1, min(p.M, int(4e8 / (2 * p.N * p.K))))
+    rows(1)                                   # first call starts the oracle's threads
+    R0 = max(1, min(p.M, int(2e9 / (2 * p.N * p.K))))
     t0, _ = rows(R0)
-    R = max(1, min(p.M, int(R0 * max(0.0, target_s - t0) / max(t0, 1e-6))))
+    R = max(1, min(p.M, int(R0 * target_s / max(t0, 1e-6))))
     t, vals = rows(R)
+    if t < 0.6 * target_s and R < p.M:          # one correction if the estimate was short
+        R = max(1, min(p.M, int(R * target_s / max(t, 1e-6))))
+        t, vals = rows(R)
     flop = 2.0 * R * p.N * p.K
     # the sample doubles as a parity check of the timed GPU output
     g = gpu_c[:R].astype(np.float64)

@@ -124,58 +124,115 @@ bool aligned_class(int64_t K, const void* A, int64_t lda, const void* B, int64_t
          is_aligned16(A) && is_aligned16(B) && is_aligned16(C);
 }
 
+// The K split a launch of `kd` would use for a requested split: slices are
+// whole multiples of 64 K elements and empty trailing slices are dropped, so
+// the result may be smaller than asked (1 = no split).  -1 when the instance
+// cannot split or the partial tiles would not fit the workspace.
+int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, int requested,
+                        int64_t* chunk_out) {
+  if (requested <= 1) {
+    *chunk_out = K;
+    return 1;
+  }
+  if (!kd.splitk_ok) return -1;
+  const int64_t chunk = ((K + requested - 1) / requested + 63) / 64 * 64;
+  const int64_t sk = (K + chunk - 1) / chunk;
+  *chunk_out = sk > 1 ? chunk : K;
+  if (sk <= 1) return 1;
+  const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
+  if (tiles > kMaxTiles || tiles * sk > INT32_MAX ||
+      (size_t)tiles * sk * kd.bm * kd.bn * sizeof(float) > kWsBytes)
+    return -1;
+  return sk;
+}
+
 // Built-in choice when the table has nothing close.  Small M streams B through
-// the skinny family; otherwise the largest LDS tile that still gives every CU
-// a workgroup ([P2] 正文 paragraph 3: large tiles raise reuse and lower
-// occupancy, so the tile is the largest that keeps the machine full).
+// the skinny family; otherwise the largest LDS tile that still fills a good
+// part of the machine ([P2] 正文 paragraph 3: large tiles raise reuse and
+// lower occupancy).  The thresholds come from timing every instance on
+// MI355X over the LLM projection and square shapes: one partial wave of
+// 256x256 tiles beats more waves of smaller tiles down to half a wave
+// (the chip is power-bound, so idle CUs buy clock for the busy ones), and
+// when even 128x128 tiles leave half the CUs idle, splitting K over them
+// beats smaller tiles once K is long.
 Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
   Config c;
   if (!aligned) return c;
-  (void)K;
+  const int k128 = find_kernel("dtile_128x128_w2x2_m16_s4");
+  const int64_t t128 = k128 >= 0 ? kKernels[k128].grid((int32_t)M, (int32_t)N) : 0;
+  // as many K slices of 128x128 tiles as keep every slice >= 1024 deep and
+  // the grid <= 256 workgroups (1 = no split)
+  auto split_for = [&]() {
+    int s = 1;
+    while (s < 8 && t128 * s * 2 <= 256 && K / (s * 2) >= 1024) s *= 2;
+    int64_t chunk = K;
+    return (s > 1 && effective_split(kKernels[k128], M, N, K, s, &chunk) > 1) ? s : 1;
+  };
   if (M <= 64) {
-    const char* name = M <= 16 ? "skinny_1x1_w8_u4" : M <= 32 ? "skinny_2x1_w8_u4" : "skinny_4x1_w8_u2";
+    // M <= 32: stream B through the skinny family (wider column tiles when N
+    // is large).  M <= 64 with N or K of 8192 and more: split K over 128x128
+    // tiles, whose MFMAs then do the work; otherwise skinny.
+    if (M > 32 && k128 >= 0 && (N >= 8192 || K >= 8192) && K >= 2048) {
+      const int s = split_for();
+      if (s > 1) {
+        c.kernel = k128;
+        c.splitk = s;
+        return c;
+      }
+    }
+    const char* name = M <= 16 ? (N >= 8192 ? "skinny_1x4_w4_u2" : "skinny_1x1_w4_u4")
+                       : M <= 32 ? "skinny_2x1_w8_u4" : "skinny_2x2_w4_u4";
     c.kernel = find_kernel(name);
     if (c.kernel < 0) c.kernel = kGenericKernel;
     return c;
   }
-  // Largest tile that still gives every CU a workgroup; the measured best
-  // instance of each tile size on MI355X (8192^3 / 4096^3 / LLM shapes).
-  static const char* const order[] = {"d2tile_256x256_w2x4_m16", "dtile_256x128_w2x2_m16_s4",
-                                      "dtile_128x128_w2x2_m16_s4", "tile_128x64_w2x2_m32",
-                                      "tile_64x64_w2x2_m32"};
-  const int n = (int)(sizeof(order) / sizeof(order[0]));
-  for (int t = 0; t < n; ++t) {
-    const int k = find_kernel(order[t]);
-    if (k < 0) continue;
-    c.kernel = k;
-    if (kKernels[k].grid((int32_t)M, (int32_t)N) >= 256) break;
+  const int k256 = find_kernel("d2tile_256x256_w2x4_m16");
+  const int64_t t256 = k256 >= 0 ? kKernels[k256].grid((int32_t)M, (int32_t)N) : 0;
+  if (k256 >= 0 && t256 >= 128) {
+    c.kernel = k256;
+    c.group_m = 8;
+    c.xcd = 1;
+    return c;
   }
-  c.group_m = 8;
-  c.xcd = 1;
-  // Too few output tiles to fill 256 CUs and a long K: split K over 128x128
-  // tiles (the fix-up reads back (splitk - 1) fp32 partial tiles per tile).
-  const int sk = find_kernel("dtile_128x128_w2x2_m16_s4");
-  if (sk >= 0 && K >= 1024 && kKernels[sk].grid((int32_t)M, (int32_t)N) < 192) {
-    {
-      const int64_t tiles = kKernels[sk].grid((int32_t)M, (int32_t)N);
-      int s = 1;
-      while (s < 8 && tiles * s * 2 <= 384 && K / (s * 2) >= 512) s *= 2;
-      if (s > 1 && tiles <= kMaxTiles &&
-          (size_t)tiles * s * 128 * 128 * sizeof(float) <= kWsBytes) {
-        c.kernel = sk;
-        c.splitk = s;
-        c.group_m = 1;
-        c.xcd = 0;
-      }
+  if (k128 >= 0 && t128 >= 128) {
+    c.kernel = k128;
+    c.group_m = 4;
+    c.xcd = 1;
+    return c;
+  }
+  if (k128 >= 0 && K >= 2048) {
+    const int s = split_for();
+    if (s > 1) {
+      c.kernel = k128;
+      c.splitk = s;
+      return c;
     }
   }
+  static const char* const small[] = {"tile_128x64_w2x2_m32", "tile_64x64_w2x2_m32"};
+  for (const char* name : small) {
+    const int k = find_kernel(name);
+    if (k < 0) continue;
+    c.kernel = k;
+    c.group_m = 8;
+    c.xcd = 1;
+    if (kKernels[k].grid((int32_t)M, (int32_t)N) >= 256) break;
+  }
+  return c;
+}
+
+// A table entry's split may not suit the shape it is applied to (a nearest
+// entry, or an edited table): such a split is dropped rather than failing.
+Config checked(Config c, int64_t M, int64_t N, int64_t K) {
+  int64_t chunk = K;
+  if (c.splitk > 1 && effective_split(kKernels[c.kernel], M, N, K, c.splitk, &chunk) < 1)
+    c.splitk = 1;
   return c;
 }
 
 Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
   const Key key{M, N, K, aligned ? 1 : 0};
   auto it = h->table.find(key);
-  if (it != h->table.end()) return it->second;
+  if (it != h->table.end()) return checked(it->second, M, N, K);
   // nearest tuned shape in log2(M, N, K), within a factor of two overall
   double best = 1.0 + 1e-9;
   const Config* pick = nullptr;
@@ -189,7 +246,7 @@ Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
       pick = &kv.second;
     }
   }
-  if (pick) return *pick;
+  if (pick) return checked(*pick, M, N, K);
   return heuristic(M, N, K, aligned);
 }
 
@@ -305,18 +362,12 @@ mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N,
   a.ws = h->ws;
   a.cnt = h->cnt;
   if (c.splitk > 1) {
-    if (!kd.splitk_ok || !h->ws || !h->cnt) return MI_HGEMM_ERR_UNSUPPORTED;
-    // slices of a multiple of 64 K elements; empty trailing slices are dropped
-    const int64_t chunk = ((K + c.splitk - 1) / c.splitk + 63) / 64 * 64;
-    const int64_t sk = (K + chunk - 1) / chunk;
-    const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
-    if (sk > 1) {
-      if (tiles > kMaxTiles || tiles * sk > INT32_MAX ||
-          (size_t)tiles * sk * kd.bm * kd.bn * sizeof(float) > kWsBytes)
-        return MI_HGEMM_ERR_UNSUPPORTED;
-      a.splitk = (int32_t)sk;
-      a.kchunk = (int32_t)chunk;
-    }
+    if (!h->ws || !h->cnt) return MI_HGEMM_ERR_UNSUPPORTED;
+    int64_t chunk = K;
+    const int64_t sk = effective_split(kd, M, N, K, c.splitk, &chunk);
+    if (sk < 1) return MI_HGEMM_ERR_UNSUPPORTED;
+    a.splitk = (int32_t)sk;
+    a.kchunk = (int32_t)chunk;
   }
   const hipError_t e = kd.launch(a, stream);
   if (e != hipSuccess) return hip_fail(h, e);
@@ -499,7 +550,7 @@ mi_hgemm_status_t mi_hgemm_table_save(mi_hgemm_handle_t h, const char* path) {
   if (!h || !path) return MI_HGEMM_ERR_INVALID_ARG;
   FILE* f = std::fopen(path, "w");
   if (!f) return MI_HGEMM_ERR_IO;
-  bool ok = std::fprintf(f, "# arch M N K layout align kernel group_m xcd_remap us\n") > 0;
+  bool ok = std::fprintf(f, "# arch M N K layout align kernel group_m xcd_remap us split_k\n") > 0;
   {
     std::lock_guard<std::mutex> lk(h->mu);
     for (const auto& kv : h->table) ok = ok && write_entry(f, kv.first, kv.second);
@@ -523,6 +574,44 @@ struct Scratch {
 double median(std::vector<double> v) {
   std::sort(v.begin(), v.end());
   return v.empty() ? 0.0 : v[v.size() / 2];
+}
+
+struct TimingStream {
+  hipStream_t s = nullptr;
+  ~TimingStream() {
+    if (s) (void)hipStreamDestroy(s);
+  }
+};
+
+// Capture `reps` launches of one candidate on stream `ts` into a graph and
+// time 5 replays; appends microseconds per launch to `trials`.
+hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t N, int64_t K,
+                        const void* A, const void* B, void* C, int64_t ldc, int reps,
+                        hipStream_t ts, hipEvent_t ev0, hipEvent_t ev1,
+                        std::vector<double>& trials) {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipError_t e = hipStreamBeginCapture(ts, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return e;
+  mi_hgemm_status_t st = MI_HGEMM_OK;
+  for (int r = 0; r < reps && st == MI_HGEMM_OK; ++r)
+    st = launch(h, cand, M, N, K, A, K, B, K, C, ldc, ts);
+  e = hipStreamEndCapture(ts, &graph);
+  if (e == hipSuccess && st != MI_HGEMM_OK) e = hipErrorLaunchFailure;
+  if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipGraphLaunch(exec, ts);  // warm-up replay
+  for (int t = 0; t < 5 && e == hipSuccess; ++t) {
+    float ms = 0.f;
+    if ((e = hipEventRecord(ev0, ts)) != hipSuccess) break;
+    if ((e = hipGraphLaunch(exec, ts)) != hipSuccess) break;
+    if ((e = hipEventRecord(ev1, ts)) != hipSuccess) break;
+    if ((e = hipEventSynchronize(ev1)) != hipSuccess) break;
+    if ((e = hipEventElapsedTime(&ms, ev0, ev1)) != hipSuccess) break;
+    trials.push_back(1000.0 * ms / reps);
+  }
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  return e;
 }
 
 }  // namespace
@@ -566,6 +655,12 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     return hip_fail(h, e);
   }
 
+  TimingStream ts;
+  if ((e = hipStreamCreateWithFlags(&ts.s, hipStreamNonBlocking)) != hipSuccess) {
+    (void)hipEventDestroy(ev0);
+    (void)hipEventDestroy(ev1);
+    return hip_fail(h, e);
+  }
   const bool heuristic_only = (flags & MI_HGEMM_TUNE_HEURISTIC) != 0;
   const Config start = heuristic(M, N, K, true);
   std::vector<Config> cands;
@@ -632,7 +727,9 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
       break;
     }
     if (bad != 0) continue;  // a wrong candidate never wins
-    // time: size the repeat count to ~1 ms per trial, median of 5 trials
+    // time: `reps` launches (about 1 ms of work) captured in one graph on a
+    // private stream and replayed, so that the figure is device time rather
+    // than host launch cost; the median of 5 replays is kept
     float ms = 0.f;
     (void)hipEventRecord(ev0, s);
     (void)launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
@@ -642,16 +739,9 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
       break;
     }
     (void)hipEventElapsedTime(&ms, ev0, ev1);
-    int reps = (int)std::min(200.0, std::max(1.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
+    const int reps = (int)std::min(200.0, std::max(1.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
     std::vector<double> trials;
-    for (int t = 0; t < 5; ++t) {
-      (void)hipEventRecord(ev0, s);
-      for (int r = 0; r < reps; ++r) (void)launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
-      (void)hipEventRecord(ev1, s);
-      if ((e = hipEventSynchronize(ev1)) != hipSuccess) break;
-      (void)hipEventElapsedTime(&ms, ev0, ev1);
-      trials.push_back(1000.0 * ms / reps);
-    }
+    e = time_replays(h, cand, M, N, K, a.p, b.p, c.p, ldc, reps, ts.s, ev0, ev1, trials);
     if (e != hipSuccess) {
       result = hip_fail(h, e);
       break;

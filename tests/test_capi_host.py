@@ -146,7 +146,39 @@ def test_heuristic_picks_by_shape(inspect_handle):
     small = names[plan(h, 256, 256, 256)[1]]
     assert "tile_" in small and small != "d2tile_256x256_w2x4_m16"
     r = plan(h, 256, 4096, 4096)                     # 16 large tiles: split K over 128x128 tiles
-    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] > 1
+    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 4
+    # half a wave or more of 256x256 tiles keeps the large tile
+    assert names[plan(h, 1024, 14336, 4096)[1]] == "d2tile_256x256_w2x4_m16"
+    # fewer: 128x128 tiles while there are 128 of them, unsplit
+    r = plan(h, 256, 11008, 4096)
+    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 1
+    # M = 64: split K for wide or deep shapes, skinny otherwise
+    r = plan(h, 64, 11008, 4096)
+    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 2
+    assert names[plan(h, 64, 4096, 4096)[1]] == "skinny_2x2_w4_u4"
+    assert names[plan(h, 16, 14336, 4096)[1]] == "skinny_1x4_w4_u2"
+    # short K: no split, small tiles fill the machine instead
+    r = plan(h, 256, 4096, 1024)
+    assert r[4] == 1 and names[r[1]] == "tile_64x64_w2x2_m32"
+
+
+def test_nearest_table_entry_drops_a_split_that_does_not_fit(tmp_path, monkeypatch):
+    """A nearest-shape entry's K split is checked against the shape it serves:
+    partial tiles beyond the workspace fall back to no split, not an error."""
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    p = tmp_path / "t.tsv"
+    # 256x128 tiles: 32 x 112 tiles x 8 slices x 128 KiB = 3.5 GiB >> 64 MiB workspace
+    p.write_text("gfx950 8192 14336 4096 TN a16 dtile_256x128_w2x2_m16_s4 1 0 1.0 8\n")
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK
+    try:
+        names = mh.kernel_names()
+        r = plan(h, 8192, 14336, 4096)
+        assert names[r[1]] == "dtile_256x128_w2x2_m16_s4" and r[4] == 1
+        r = plan(h, 8192, 14336, 6144)                # nearest entry, same verdict
+        assert names[r[1]] == "dtile_256x128_w2x2_m16_s4" and r[4] == 1
+    finally:
+        mh.mi_hgemm_destroy(h)
 
 
 def test_table_split_k_column(tmp_path, monkeypatch):
