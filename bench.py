@@ -2,7 +2,8 @@
 """Benchmark of the TN half-precision GEMM on one MI355X.
 
 One step = one ``mi_hgemm_run`` over the workload's synthetic operands (already
-resident in HBM), through the library's normal dispatch.  By default the
+resident in HBM), through the library's normal dispatch (or a forced instance with
+``--kernel``, for per-instance counter runs).  By default the
 operands rotate over enough copies that every call reads A and B from HBM
 rather than from the 256 MiB MALL ("cold"); ``--warm`` reuses one set.
 
@@ -13,6 +14,7 @@ sample of the same product on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload square|tiny|small|llm_MxNxK]
                     [--mnk M_N_K] [--warm] [--no-cpu-baseline] [--all-configs OUT.jsonl]
+                    [--kernel NAME [--group-m G] [--xcd-remap X] [--split-k S]]
 """
 from __future__ import annotations
 
@@ -48,6 +50,11 @@ def parse():
                     help="target wall time of the oracle sample")
     ap.add_argument("--all-configs", default=None,
                     help="also time every named workload and write JSON lines here")
+    ap.add_argument("--kernel", default=None,
+                    help="force this compiled instance (by name) instead of the dispatcher's choice")
+    ap.add_argument("--group-m", type=int, default=1, help="raster group height with --kernel")
+    ap.add_argument("--xcd-remap", type=int, default=0, choices=(0, 1), help="XCD remap with --kernel")
+    ap.add_argument("--split-k", type=int, default=1, help="K split with --kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -127,15 +134,16 @@ class Workload:
         torch.cuda.synchronize()
 
 
-def time_steps(lib, wl, steps, warmup):
-    """Warm up, then time exactly `steps` launches bracketed by synchronisations.
-    Returns (ms per step, mean per-launch ms from event pairs, wall s)."""
+def time_steps(run, wl, steps, warmup):
+    """Warm up, then time exactly `steps` launches of run(a, b, c) bracketed by
+    synchronisations.  Returns (ms per step, mean per-launch ms from event pairs,
+    wall s, per-launch ms)."""
     import torch
     sets = wl.sets
     n = len(sets)
     for i in range(warmup):
         a, b, c = sets[i % n]
-        lib.run(a, b, c)
+        run(a, b, c)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -147,7 +155,7 @@ def time_steps(lib, wl, steps, warmup):
     for i in range(steps):
         a, b, c = sets[i % n]
         ev[i][0].record(stream)
-        lib.run(a, b, c)
+        run(a, b, c)
         ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -224,11 +232,19 @@ def torch_matmul_context(wl, steps=20):
     return round(wl.p.flops / (ms * 1e-3) / 1e12, 2), round(ms * 1e3, 2)
 
 
-def measure(lib, p, steps, warmup, cold, with_torch=False):
+def measure(lib, p, steps, warmup, cold, with_torch=False, force=None):
+    """force: None (the library's dispatch) or (kernel name, group_m, xcd_remap, split_k)."""
     wl = Workload(p, cold)
     a, b, c = wl.sets[0]
-    kernel, gm, xcd, sk = lib.plan(a, b, c)
-    ms, launch_ms, wall, per = time_steps(lib, wl, steps, warmup)
+    if force is None:
+        kernel, gm, xcd, sk = lib.plan(a, b, c)
+        run = lib.run
+    else:
+        kernel, gm, xcd, sk = force
+
+        def run(a, b, c):
+            lib.run_kernel(kernel, a, b, c, group_m=gm, xcd_remap=xcd, split_k=sk)
+    ms, launch_ms, wall, per = time_steps(run, wl, steps, warmup)
     rec = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "kernel": kernel, "group_m": gm,
            "xcd_remap": xcd, "split_k": sk, "cache": "cold" if cold else "warm", "sets": len(wl.sets),
            "ms_per_step": ms, "us_per_call": round(launch_ms * 1e3, 3),
@@ -279,7 +295,10 @@ def main():
                 torch.cuda.empty_cache()
 
     p = problem_for(args.workload, args.mnk)
-    rec, wl = measure(lib, p, args.steps, args.warmup, cold, with_torch=True)
+    force = None
+    if args.kernel:
+        force = (args.kernel, args.group_m, args.xcd_remap, args.split_k)
+    rec, wl = measure(lib, p, args.steps, args.warmup, cold, with_torch=True, force=force)
     out = {
         "metric": METRIC,
         "value": rec["tflops"],
@@ -297,7 +316,7 @@ def main():
                    "accumulate": "fp32", "inputs": f"{p.kind} a*{p.a_scale:.6g} b*{p.b_scale:.6g} seed {p.seed}",
                    "cache": rec["cache"], "operand_sets": rec["sets"], "kernel": rec["kernel"],
                    "group_m": rec["group_m"], "xcd_remap": rec["xcd_remap"],
-                   "split_k": rec["split_k"],
+                   "split_k": rec["split_k"], "dispatch": "forced" if args.kernel else "library",
                    "us_per_call": rec["us_per_call"], "us_per_call_median": rec["us_per_call_median"],
                    "parallelism": "none (1 GPU)"},
         "roofline": rec["roofline"],

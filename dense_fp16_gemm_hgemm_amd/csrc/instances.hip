@@ -151,6 +151,26 @@ hipError_t launch_fill_small_int(void* X, int64_t n, uint32_t seed, hipStream_t 
   return hipGetLastError();
 }
 
+// Values uniform in (-scale, scale) with full random mantissas: timing
+// operands whose switching activity (and so power draw and clock) matches
+// real data, unlike the small integers used for the exactness check.
+__global__ void fill_uniform_kernel(_Float16* X, int64_t n, uint32_t seed, float scale) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t h = mix32((uint32_t)t ^ mix32(seed ^ (uint32_t)(t >> 32)));
+    X[t] = (_Float16)(scale * ((float)(h >> 8) * (2.0f / 16777216.0f) - 1.0f));
+  }
+}
+
+hipError_t launch_fill_uniform(void* X, int64_t n, uint32_t seed, float scale, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_uniform_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<_Float16*>(X), n, seed, scale);
+  return hipGetLastError();
+}
+
 __global__ void count_mismatch_kernel(const uint16_t* X, const uint16_t* Y, int32_t M, int32_t N,
                                       int64_t ld, int* count) {
   const int64_t total = (int64_t)M * N;

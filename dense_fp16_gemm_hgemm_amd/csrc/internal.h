@@ -52,6 +52,7 @@ hipError_t launch_zero_fill(void* C, int64_t ldc, int32_t M, int32_t N, hipStrea
 // Fills an n-element binary16 buffer with integers in [-4, 4] from a hash of
 // (seed, index); used for the tuner's scratch operands.
 hipError_t launch_fill_small_int(void* X, int64_t n, uint32_t seed, hipStream_t s);
+hipError_t launch_fill_uniform(void* X, int64_t n, uint32_t seed, float scale, hipStream_t s);
 
 // Counts the elements of the M x N blocks (leading dimension ld) of two binary16
 // arrays whose bit patterns differ, +0 and -0 counted equal; the count is

@@ -633,15 +633,22 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t ldc = (N + 7) / 8 * 8;
 
-  Scratch a, b, c, cref, cnt;
+  // a, b: small integers, for the bit-exact check; ta, tb: random mantissas
+  // scaled by 1/sqrt(K), for timing (the clock depends on the data)
+  Scratch a, b, ta, tb, c, cref, cnt;
   hipError_t e;
   if ((e = hipMalloc(&a.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&b.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&ta.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&tb.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&c.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cref.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cnt.p, sizeof(int))) != hipSuccess) return hip_fail(h, e);
   if ((e = mihg::launch_fill_small_int(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
   if ((e = mihg::launch_fill_small_int(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
+  const float tscale = 1.0f / std::sqrt((float)K);
+  if ((e = mihg::launch_fill_uniform(ta.p, M * K, 0x9abcu, tscale, s)) != hipSuccess) return hip_fail(h, e);
+  if ((e = mihg::launch_fill_uniform(tb.p, N * K, 0xdef0u, tscale, s)) != hipSuccess) return hip_fail(h, e);
 
   // Reference result: the element-wise instance.
   Config ref;
@@ -732,7 +739,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     // than host launch cost; the median of 5 replays is kept
     float ms = 0.f;
     (void)hipEventRecord(ev0, s);
-    (void)launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
+    (void)launch(h, cand, M, N, K, ta.p, K, tb.p, K, c.p, ldc, s);
     (void)hipEventRecord(ev1, s);
     if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
       result = hip_fail(h, e);
@@ -741,7 +748,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     (void)hipEventElapsedTime(&ms, ev0, ev1);
     const int reps = (int)std::min(200.0, std::max(1.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
     std::vector<double> trials;
-    e = time_replays(h, cand, M, N, K, a.p, b.p, c.p, ldc, reps, ts.s, ev0, ev1, trials);
+    e = time_replays(h, cand, M, N, K, ta.p, tb.p, c.p, ldc, reps, ts.s, ev0, ev1, trials);
     if (e != hipSuccess) {
       result = hip_fail(h, e);
       break;

@@ -113,13 +113,17 @@ mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_
                                void* C, int64_t ldc, mi_hgemm_layout_t layout, void* stream);
 
 /*
- * Search the compiled instances and raster settings for the shape (M, N, K)
- * in the 16-byte alignment class: each valid candidate is timed with HIP
- * events on library-owned scratch operands (small integers, so every correct
- * candidate gives bit-identical C) and checked against the element-wise
- * instance; the fastest correct one becomes the handle's entry for the shape.
+ * Search the compiled instances, raster settings and K splits for the shape
+ * (M, N, K) in the 16-byte alignment class.  Each candidate is first run on
+ * library-owned small-integer operands, on which every correct candidate gives
+ * C bit-identical to the element-wise instance's (a candidate that differs is
+ * discarded); it is then timed on operands with random mantissas scaled by
+ * 1/sqrt(K) (the clock under load depends on the data), as the median of 5
+ * replays of a captured graph of repeated launches on a private stream.  The
+ * fastest correct one becomes the handle's entry for the shape.
  * With MI_HGEMM_TUNE_PERSIST the entry is appended to the handle's table file.
- * Synchronises `stream`.  Allocates scratch (freed before returning).
+ * Synchronises `stream`.  Allocates scratch (two operand sets and two
+ * outputs, freed before returning).
  * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
  */
 mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
