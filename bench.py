@@ -232,7 +232,33 @@ def torch_matmul_context(wl, steps=20):
     return round(wl.p.flops / (ms * 1e-3) / 1e12, 2), round(ms * 1e3, 2)
 
 
-def measure(lib, p, steps, warmup, cold, with_torch=False, force=None):
+def graph_us(fn, wl, reps):
+    """Device time per call: `reps` calls of fn(a, b, c), rotating over the
+    workload's operand sets, captured in one graph and replayed."""
+    import torch
+    sets = wl.sets
+    fn(*sets[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(reps):
+                fn(*sets[i % len(sets)])
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del g
+    return us
+
+
+def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_time=False):
     """force: None (the library's dispatch) or (kernel name, group_m, xcd_remap, split_k)."""
     wl = Workload(p, cold)
     a, b, c = wl.sets[0]
@@ -253,6 +279,20 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None):
            "roofline": roofline(p, launch_ms, kernel, p.name)}
     if with_torch:
         rec["torch_matmul_tflops"], rec["torch_matmul_us"] = torch_matmul_context(wl)
+    if device_time:
+        # the stream figures above include the host's launch path, which exceeds
+        # the kernel for small shapes; graph replay gives the device time
+        reps = min(2048, max(len(wl.sets), 20, int(20000 / max(launch_ms * 1e3, 1.0))))
+        dus = graph_us(run, wl, reps)
+        rec["device_us_per_call"] = round(dus, 3)
+        rec["device_tflops"] = round(p.flops / (dus * 1e-6) / 1e12, 3)
+        rec["device_roofline"] = roofline(p, dus * 1e-3, kernel, p.name)
+        if with_torch:
+            import torch
+
+            def tm(a, b, c):
+                torch.matmul(a, b.t(), out=c)
+            rec["torch_device_us_per_call"] = round(graph_us(tm, wl, reps), 3)
     return rec, wl
 
 
@@ -286,11 +326,13 @@ def main():
                 if p.kind != "randn":
                     continue
                 for c in (True, False):
-                    rec, _ = measure(lib, p, max(20, args.steps // 2), 5, c, with_torch=True)
+                    rec, _ = measure(lib, p, max(20, args.steps // 2), 5, c, with_torch=True,
+                                     device_time=True)
                     f.write(json.dumps(rec) + "\n")
                     f.flush()
-                    print(f"# {p.name} {rec['cache']}: {rec['us_per_call']} us "
-                          f"{rec['tflops']} TFLOP/s ({rec['kernel']}) torch {rec['torch_matmul_us']} us",
+                    print(f"# {p.name} {rec['cache']}: device {rec['device_us_per_call']} us "
+                          f"({rec['kernel']} s{rec['split_k']}) torch {rec['torch_device_us_per_call']} us; "
+                          f"stream {rec['us_per_call']} us, torch {rec['torch_matmul_us']} us",
                           file=sys.stderr, flush=True)
                 torch.cuda.empty_cache()
 

@@ -90,7 +90,7 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
    1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
 #define SKINNY_DESC(FM, FN, W, U)                                                          \
   {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
-   W * 16 * FM * 16 * FN * 4, 0, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
+   W * 16 * FM * 16 * FN * 4, 1, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
 
 const KernelDesc kKernels[] = {
     // element-wise instance: any alignment, any leading dimensions (must stay first)

@@ -360,12 +360,15 @@ tile_kernel(GemmArgs p) {
 // buffer_load_dwordx4 ... lds (global -> LDS without passing through VGPRs)
 // into a ring of S LDS stages, one wave per SIMD, large wave tiles.
 //
-// LDS layout: 64-byte rows (32 halves, 4 chunks of 16 bytes), chunk index
-// XORed with (row >> 2) & 3.  One DMA instruction of a wave fills a 1 KiB
-// block = 16 rows; lane l lands on row l/4, physical chunk l%4, so it loads
-// logical chunk (l%4) ^ (l/16) -- the same for every block, one offset
-// register per operand.  A 16-row fragment read at one logical chunk touches
-// 16 distinct (row mod 4, chunk) bank groups: conflict-free with 64 banks.
+// LDS layout: row pairs.  A tile row holds 32 halves (64 bytes, 4 chunks of
+// 16 bytes); LDS row R (128 bytes) holds tile rows 2R and 2R+1 as logical
+// chunks c = 4*(row & 1) + k-chunk, stored at physical chunk c ^ (R & 7).
+// (Plain 64-byte rows with the chunk XORed by (row >> 2) & 3 measured 4 bank
+// conflict cycles per fragment read on gfx950; this layout measured none.)
+// One DMA instruction of a wave fills a 1 KiB block = 8 LDS rows = 16 tile
+// rows; lane l lands on LDS row l/8, physical chunk l%8, so it loads logical
+// chunk (l%8) ^ (l/8) -- the same for every block, one offset register per
+// operand.
 //
 // Pipeline (trip k): issue the DMA of tile k+S-1 into the stage tile k-1 used;
 // read tile k+1's fragments (published one barrier ago) into the second
@@ -484,7 +487,8 @@ dtile_kernel(GemmArgs p) {
   // an LDS store, so the workgroup barrier's fence does not drain every copy
   // in flight; completion is tracked explicitly with vmcnt (wait_dma).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int drow = lane >> 2, dchunk = (lane & 3) ^ (lane >> 4);
+  const int dlc = (lane & 7) ^ (lane >> 3);                 // logical chunk of LDS row l/8
+  const int drow = 2 * (lane >> 3) + (dlc >> 2), dchunk = dlc & 3;  // tile row, k-chunk
   const uint32_t a_voff = (uint32_t)(drow * lda * 2 + dchunk * 16);
   const uint32_t b_voff = (uint32_t)(drow * ldb * 2 + dchunk * 16);
   const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
@@ -525,15 +529,17 @@ dtile_kernel(GemmArgs p) {
     }
   };
 
-  // fragment reads: row base + per-lane physical chunk; fm / fn / step are immediates
+  // fragment reads: LDS row of the lane's tile row + physical chunk; fm / fn /
+  // step are immediates.  Fragment blocks start at multiples of 16 tile rows
+  // (8 LDS rows), so the swizzle term of tile row frow is (frow / 2) & 7.
   const int frow = lane % MF, fq = lane / MF;
   int fa_off[KSTEPS], fb_off[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    const int q = s * (MM::KI / 8) + fq;            // logical chunk
-    const int phys = q ^ ((frow >> 2) & 3);          // block bases are multiples of 16 rows
-    fa_off[s] = (wm * WTM + frow) * kDRow + phys * 8;
-    fb_off[s] = (BM + wn * WTN + frow) * kDRow + phys * 8;
+    const int c = 4 * (frow & 1) + s * (MM::KI / 8) + fq;  // logical chunk in the LDS row
+    const int in_row = (frow >> 1) * (2 * kDRow) + ((c ^ ((frow >> 1) & 7)) * 8);
+    fa_off[s] = (wm * WTM) * kDRow + in_row;
+    fb_off[s] = (BM + wn * WTN) * kDRow + in_row;
   }
   h8 fa[2][KSTEPS][FM], fb[2][KSTEPS][FN];
   auto fread = [&](const _Float16* stage, int buf) {
@@ -867,10 +873,12 @@ d2tile_kernel(GemmArgs p) {
   constexpr int NM = FM * FN, NR = FM + FN;
   // One half trip: the NM MFMAs of step S_MFMA (when DO_MFMA), with the
   // copies of the next tile (when COPY) and the NR fragment reads of step
-  // S_READ spread over its first three quarters; copies and reads alternate
-  // while copies last.
+  // S_READ spread evenly over its MFMA slots; copies and reads alternate
+  // while copies last.  (Spreading them over the whole half measured ~1.5%
+  // faster on 8192^3 than packing them into its first three quarters, and
+  // issuing every copy first was ~3% slower.)
   auto half = [&](auto DO_MFMA, auto COPY, auto S_MFMA, auto S_READ, int rst, int kcopy, int wst) {
-    constexpr int SPAN = (NM * 3) / 4;
+    constexpr int SPAN = NM;
     constexpr int nd = decltype(COPY)::value ? ND : 0;
     constexpr int nx = nd + NR;
     constexpr int sm = decltype(S_MFMA)::value, sr = decltype(S_READ)::value;
@@ -1061,7 +1069,10 @@ generic_kernel(GemmArgs p) {
 // with the next group's loads issued before the current group's MFMAs.  The
 // per-wave fp32 partial tiles are summed through LDS in wave order (so the
 // result does not depend on timing) and converted once.  B, the large operand
-// for these shapes, is read exactly once; A is re-read from L2.
+// for these shapes, is read exactly once; A is re-read from L2 by every column
+// tile, so wide column tiles split over K (workgroup = tile x slice, the same
+// device-coherent fix-up as the direct-to-LDS family, slices summed in order)
+// fill the device while cutting that re-read.
 // Requires the 16-byte alignment class.
 template <int FM, int FN, int WAVES, int UNROLL>
 __global__ void __launch_bounds__(64 * WAVES)
@@ -1070,10 +1081,16 @@ skinny_kernel(GemmArgs p) {
   constexpr int BM = 16 * FM, BN = 16 * FN;
   __shared__ __attribute__((aligned(16))) float red[WAVES][BM * BN];
 
+  __shared__ int s_last;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, N = p.N, K = p.K;
   const int tiles_m = (M + BM - 1) / BM;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  // split-K: workgroup id = tile * splitk + slice; slice s covers K range
+  // [s * kchunk, min(K, (s + 1) * kchunk)), kchunk a multiple of 64
+  const int splitk = p.splitk;
+  const int tile_id = blockIdx.x / splitk, slice = blockIdx.x - tile_id * splitk;
+  const int tm = tile_id % tiles_m, tn = tile_id / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const _Float16* A = static_cast<const _Float16*>(p.A);
   const _Float16* B = static_cast<const _Float16*>(p.B);
@@ -1090,8 +1107,10 @@ skinny_kernel(GemmArgs p) {
   for (int fn = 0; fn < FN; ++fn) b_off[fn] = (uint32_t)((fn * 16 + r) * p.ldb * 2 + q * 16);
 
   const int steps = (K + MM::KI - 1) / MM::KI;
-  const int s_begin = (int)((int64_t)steps * wave / WAVES);
-  const int s_end = (int)((int64_t)steps * (wave + 1) / WAVES);
+  const int sl_lo = splitk > 1 ? slice * (p.kchunk / MM::KI) : 0;
+  const int sl_hi = splitk > 1 ? min(steps, (slice + 1) * (p.kchunk / MM::KI)) : steps;
+  const int s_begin = sl_lo + (int)((int64_t)(sl_hi - sl_lo) * wave / WAVES);
+  const int s_end = sl_lo + (int)((int64_t)(sl_hi - sl_lo) * (wave + 1) / WAVES);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -1146,24 +1165,75 @@ skinny_kernel(GemmArgs p) {
       for (int v = 0; v < 4; ++v)
         red[wave][(fm * 16 + r) * BN + fn * 16 + 4 * q + v] = acc[fm][fn][v];
   __syncthreads();
+  constexpr int NT = 64 * WAVES, NE = BM * BN / 4, EPT = (NE + NT - 1) / NT;
+  f32x4 sum[EPT];
+#pragma unroll
+  for (int t = 0; t < EPT; ++t) {
+    const int e = tid + t * NT;
+    if (e < NE) {
+      const int ii = (e * 4) / BN, jj = (e * 4) % BN;
+      f32x4 s = *reinterpret_cast<const f32x4*>(&red[0][ii * BN + jj]);
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) s += *reinterpret_cast<const f32x4*>(&red[w][ii * BN + jj]);
+      sum[t] = s;
+    }
+  }
+  if (splitk > 1) {
+    // Fix-up as in the direct-to-LDS family: partials stored and read with
+    // device scope (SC1), the counter a relaxed device-scope atomic taken
+    // after every wave's stores are acknowledged; the last slice sums the
+    // slices in order 0..splitk-1, writes C and resets the counter.
+    const auto rsw = make_rsrc(reinterpret_cast<const f32x4*>(p.ws) + (int64_t)tile_id * splitk * NE,
+                               (uint32_t)(splitk * NE * 16));
+#pragma unroll
+    for (int t = 0; t < EPT; ++t) {
+      const int e = tid + t * NT;
+      if (e < NE)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum[t]), rsw,
+                                               (uint32_t)((slice * NE + e) * 16), 0, kDeviceScope);
+    }
+    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));  // vmcnt(0): partial stores acknowledged
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&p.cnt[tile_id], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == splitk - 1;
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int t = 0; t < EPT; ++t) {
+      const int e = tid + t * NT;
+      if (e < NE) {
+        f32x4 total = {0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < splitk; ++s2)
+          total += s2 == slice
+                       ? sum[t]
+                       : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rsw, (uint32_t)((s2 * NE + e) * 16), 0,
+                                                       kDeviceScope));
+        sum[t] = total;
+      }
+    }
+    if (tid == 0)
+      __hip_atomic_store(&p.cnt[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   _Float16* Cw = C + m0 * p.ldc;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * p.ldc * 2));
   const bool n_quads = (N & 3) == 0;
-  for (int e = tid; e < BM * BN / 4; e += 64 * WAVES) {
+#pragma unroll
+  for (int t = 0; t < EPT; ++t) {
+    const int e = tid + t * NT;
+    if (e >= NE) continue;
     const int ii = (e * 4) / BN, jj = (e * 4) % BN;
     const int j = n0 + jj;
-    f32x4 s = *reinterpret_cast<const f32x4*>(&red[0][ii * BN + jj]);
-#pragma unroll
-    for (int w = 1; w < WAVES; ++w) s += *reinterpret_cast<const f32x4*>(&red[w][ii * BN + jj]);
     h4 o;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] = (_Float16)s[t];
+    for (int q4 = 0; q4 < 4; ++q4) o[q4] = (_Float16)sum[t][q4];
     const uint32_t off = (uint32_t)((ii * p.ldc + j) * 2);
     if (n_quads) {
       buf_store8(rsc, j < N ? off : kOOB, o);
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) buf_store2(rsc, j + t < N ? off + 2 * t : kOOB, o[t]);
+      for (int q4 = 0; q4 < 4; ++q4) buf_store2(rsc, j + q4 < N ? off + 2 * q4 : kOOB, o[q4]);
     }
   }
 }
@@ -1210,7 +1280,8 @@ int64_t grid_tile(int32_t M, int32_t N) {
 
 template <int FM, int FN, int WAVES, int UNROLL>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)((a.M + 16 * FM - 1) / (16 * FM)) * ((a.N + 16 * FN - 1) / (16 * FN));
+  const int64_t g =
+      (int64_t)((a.M + 16 * FM - 1) / (16 * FM)) * ((a.N + 16 * FN - 1) / (16 * FN)) * a.splitk;
   hipLaunchKernelGGL((skinny_kernel<FM, FN, WAVES, UNROLL>), dim3((unsigned)g), dim3(64 * WAVES),
                      0, s, a);
   return hipGetLastError();

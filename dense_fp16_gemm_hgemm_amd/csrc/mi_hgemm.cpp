@@ -671,6 +671,20 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   const bool heuristic_only = (flags & MI_HGEMM_TUNE_HEURISTIC) != 0;
   const Config start = heuristic(M, N, K, true);
   std::vector<Config> cands;
+  // split K when the output tiles alone leave CUs idle
+  auto add_splits = [&](int k) {
+    const KernelDesc& kd = kKernels[k];
+    const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
+    if (!kd.splitk_ok || !h->ws || tiles >= 256) return;
+    for (int s = 2; s <= 16; s *= 2) {
+      int64_t chunk = K;
+      if (K / s < 256 || tiles * s > 1024 || effective_split(kd, M, N, K, s, &chunk) < s) break;
+      Config c;
+      c.kernel = k;
+      c.splitk = s;
+      cands.push_back(c);
+    }
+  };
   for (int k = 0; k < kNumKernels; ++k) {
     const KernelDesc& kd = kKernels[k];
     if (!kd.aligned) continue;
@@ -685,24 +699,13 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
         c.xcd = r[1];
         cands.push_back(c);
       }
-      // split K when the output tiles alone leave CUs idle
-      const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
-      if (kd.splitk_ok && h->ws && tiles < 256) {
-        for (int s = 2; s <= 16; s *= 2) {
-          if (K / s < 256 || tiles * s > 1024 ||
-              (size_t)tiles * s * kd.bm * kd.bn * sizeof(float) > kWsBytes)
-            break;
-          Config c;
-          c.kernel = k;
-          c.splitk = s;
-          cands.push_back(c);
-        }
-      }
+      add_splits(k);
     } else {
       if (heuristic_only && M > 128) continue;
       Config c;
       c.kernel = k;
       cands.push_back(c);
+      add_splits(k);
     }
   }
   if (std::find_if(cands.begin(), cands.end(), [&](const Config& c) {
