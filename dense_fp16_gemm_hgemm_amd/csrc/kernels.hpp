@@ -1063,9 +1063,9 @@ generic_kernel(GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // Skinny family (small M): no LDS staging of operands.  Each workgroup owns a
-// (16*FM) x (16*FN) output tile; its WAVES waves split the K range into
-// contiguous slices and stream A and B fragments straight from global memory
-// into registers in the 16x16x32 MFMA layout, UNROLL k-steps per load group,
+// (16*FM) x (16*FN) output tile; its WAVES waves take turns over groups of
+// UNROLL k-steps and stream A and B fragments straight from global memory
+// into registers in the 16x16x32 MFMA layout, one group per load,
 // with the next group's loads issued before the current group's MFMAs.  The
 // per-wave fp32 partial tiles are summed through LDS in wave order (so the
 // result does not depend on timing) and converted once.  B, the large operand
@@ -1106,11 +1106,13 @@ skinny_kernel(GemmArgs p) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) b_off[fn] = (uint32_t)((fn * 16 + r) * p.ldb * 2 + q * 16);
 
+  // The slice's k-steps form groups of UNROLL; wave w takes groups w,
+  // w + WAVES, ...  so the waves of a workgroup stream neighbouring stretches
+  // of the same B rows at the same time.
   const int steps = (K + MM::KI - 1) / MM::KI;
   const int sl_lo = splitk > 1 ? slice * (p.kchunk / MM::KI) : 0;
   const int sl_hi = splitk > 1 ? min(steps, (slice + 1) * (p.kchunk / MM::KI)) : steps;
-  const int s_begin = sl_lo + (int)((int64_t)(sl_hi - sl_lo) * wave / WAVES);
-  const int s_end = sl_lo + (int)((int64_t)(sl_hi - sl_lo) * (wave + 1) / WAVES);
+  const int ngroups = (sl_hi - sl_lo + UNROLL - 1) / UNROLL;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -1126,7 +1128,7 @@ skinny_kernel(GemmArgs p) {
     for (int u = 0; u < UNROLL; ++u) {
       const int s = s0 + u;
       const int k = s * MM::KI;
-      const bool kin = s < s_end && k + q * 8 < K;
+      const bool kin = s < sl_hi && k + q * 8 < K;
       const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) af[buf][u][fm] = buf_load16(rsa, kin ? a_off[fm] + kb : kOOB);
@@ -1144,16 +1146,16 @@ skinny_kernel(GemmArgs p) {
           acc[fm][fn] = MM::mma(bf[buf][u][fn], af[buf][u][fm], acc[fm][fn]);
   };
 
-  if (s_begin < s_end) {
-    load(0, s_begin);
-    int s = s_begin;
-    for (; s + UNROLL < s_end; s += 2 * UNROLL) {
-      load(1, s + UNROLL);
+  int g = wave;
+  if (g < ngroups) {
+    load(0, sl_lo + g * UNROLL);
+    for (; g + WAVES < ngroups; g += 2 * WAVES) {
+      load(1, sl_lo + (g + WAVES) * UNROLL);
       compute(0);
-      load(0, s + 2 * UNROLL);  // past s_end: every slot reads as 0
+      load(0, sl_lo + (g + 2 * WAVES) * UNROLL);  // past the slice: every slot reads as 0
       compute(1);
     }
-    if (s < s_end) compute(0);
+    if (g < ngroups) compute(0);
   }
 
   // partial tiles -> LDS, summed in wave order

@@ -340,3 +340,58 @@ def test_split_k_dispatch_randn_deterministic(lib):
         assert np.array_equal(host(lib.run(dA, dB)).view(np.uint16), first.view(np.uint16))
     r, c = sample_indices(p.M, p.N, 4096, seed=1)
     check_tolerance(first[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
+
+
+# --- the shape sweep and maximum sizes -------------------------------------------------------
+
+def _sweep_sample():
+    """Every 10th problem of the 1000-problem sweep whose operands stay below 2^26
+    elements each (the seeded generator then runs in seconds), 40 at most."""
+    out = []
+    for i, p in enumerate(inputs.sweep(1000)):
+        if i % 10 == 0 and p.M * p.K <= (1 << 26) and p.N * p.K <= (1 << 26):
+            out.append(p)
+    return out[:40]
+
+
+@pytest.mark.parametrize("p", _sweep_sample(), ids=lambda p: p.name)
+def test_shape_sweep_sample(lib, p):
+    """Sweep problems through the dispatcher (table, nearest entry or heuristic,
+    whichever the shape reaches): sampled entries within tolerance."""
+    A, Bt = inputs.make(p)
+    dA, dB = gpu(A), gpu(Bt)
+    log(f"sweep {p.name}: {lib.plan(dA, dB)}")
+    got = host(lib.run(dA, dB))
+    r, c = sample_indices(p.M, p.N, 2048, seed=p.seed)
+    check_tolerance(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
+
+
+@pytest.mark.parametrize("M,N", [(128, 256), (64, 64)])
+def test_long_k_integer_bitexact(lib, M, N):
+    """K = 65536: every partial sum of small integers is exact in fp32 (|sum| <
+    2^24), so the dispatcher's result (split K or not) equals the oracle's bit
+    for bit, rounding of large sums to fp16 included."""
+    K = 65536
+    A, Bt = rand_problem(M, N, K, "int", seed=M + N)
+    log(f"long K {M}x{N}x{K}: {lib.plan(gpu(A), gpu(Bt))}")
+    got = host(lib.run(gpu(A), gpu(Bt)))
+    check_bitexact(got, oracle.hgemm_tn(A, Bt), "K=65536")
+
+
+@pytest.mark.parametrize("ld,vector", [(1 << 21, True), ((1 << 21) + 8, False)])
+def test_leading_dimension_at_the_vector_limit(lib, ld, vector):
+    """lda = ldb = 2^21 is the largest leading dimension of the vector path;
+    one more multiple of 8 falls back to the element-wise instance.  Both give
+    the oracle's result (integer inputs, bit-exact)."""
+    M, N, K = 16, 64, 256
+    A, Bt = rand_problem(M, N, K, "int", seed=ld % 97)
+    a = torch.zeros((M, ld), dtype=torch.float16, device=DEV)
+    b = torch.zeros((N, ld), dtype=torch.float16, device=DEV)
+    a[:, :K] = gpu(A)
+    b[:, :K] = gpu(Bt)
+    av, bv = a[:, :K], b[:, :K]
+    name = lib.plan(av, bv)[0]
+    log(f"ld {ld}: {name}")
+    assert (name != mh.kernel_names()[0]) == vector
+    got = host(lib.run(av, bv))
+    check_bitexact(got, oracle.hgemm_tn(A, Bt), f"ld={ld}")
