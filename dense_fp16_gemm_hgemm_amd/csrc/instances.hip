@@ -47,7 +47,30 @@ namespace mihg {
   X(256, 256, 2, 4)               \
   X(256, 256, 2, 2)               \
   X(256, 128, 2, 2)               \
-  X(128, 128, 2, 2)
+  X(128, 128, 2, 2)               \
+  X(128, 64, 2, 2)                \
+  X(64, 128, 2, 2)                \
+  X(64, 64, 2, 2)
+
+// KTILE: X(BM, BN, WGM, WGN, BK, S): K step BK (128 or 256), S LDS stages
+#define MIHG_KTILE_INSTANCES(X) \
+  X(64, 64, 2, 2, 128, 2)        \
+  X(64, 64, 2, 2, 128, 3)        \
+  X(64, 64, 2, 2, 256, 2)        \
+  X(128, 64, 2, 2, 128, 2)       \
+  X(64, 128, 2, 2, 128, 2)       \
+  X(128, 128, 2, 2, 128, 2)      \
+  X(32, 64, 2, 2, 256, 2)        \
+  X(16, 64, 1, 4, 256, 2)        \
+  X(16, 64, 1, 4, 256, 3)        \
+  X(16, 64, 1, 4, 128, 3)        \
+  X(16, 128, 1, 4, 128, 3)       \
+  X(16, 16, 1, 1, 256, 3)        \
+  X(16, 32, 1, 2, 256, 3)        \
+  X(32, 64, 2, 2, 128, 3)        \
+  X(128, 64, 2, 2, 128, 3)       \
+  X(64, 128, 2, 2, 128, 3)       \
+  X(128, 128, 2, 4, 128, 2)
 
 #define MIHG_SKINNY_INSTANCES(X) \
   X(1, 1, 4, 4)                  \
@@ -61,18 +84,22 @@ namespace mihg {
   X(4, 1, 8, 2)                  \
   X(4, 2, 4, 2)
 
+
 #define INSTANTIATE_TILE(BM, BN, WGM, WGN, MF) \
   template __global__ void tile_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
 #define INSTANTIATE_DTILE(BM, BN, WGM, WGN, MF, S) \
   template __global__ void dtile_kernel<BM, BN, WGM, WGN, MF, S>(GemmArgs);
 #define INSTANTIATE_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
+  template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
 #define INSTANTIATE_SKINNY(FM, FN, W, U) \
-  template __global__ void skinny_kernel<FM, FN, W, U>(GemmArgs);
+  template __global__ void skinny_kernel<FM, FN, W, U, 2>(GemmArgs);
 template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
 MIHG_TILE_INSTANCES(INSTANTIATE_TILE)
 MIHG_DTILE_INSTANCES(INSTANTIATE_DTILE)
 MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
+MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 
 // The registry holds host launch functions, so it exists only in the host pass.
@@ -88,9 +115,13 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
    1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+#define KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
+  {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
+   WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1, &launch_ktile<BM, BN, WGM, WGN, BK / 64, S>, \
+   &grid_tile<BM, BN>},
 #define SKINNY_DESC(FM, FN, W, U)                                                          \
   {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
-   W * 16 * FM * 16 * FN * 4, 1, &launch_skinny<FM, FN, W, U>, &grid_tile<16 * FM, 16 * FN>},
+   W * 16 * FM * 16 * FN * 4, 1, &launch_skinny<FM, FN, W, U, 2>, &grid_tile<16 * FM, 16 * FN>},
 
 const KernelDesc kKernels[] = {
     // element-wise instance: any alignment, any leading dimensions (must stay first)
@@ -99,6 +130,7 @@ const KernelDesc kKernels[] = {
     MIHG_TILE_INSTANCES(TILE_DESC)
     MIHG_DTILE_INSTANCES(DTILE_DESC)
     MIHG_D2TILE_INSTANCES(D2TILE_DESC)
+    MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
 };
 

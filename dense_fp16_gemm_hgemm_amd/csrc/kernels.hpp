@@ -443,6 +443,95 @@ __device__ __forceinline__ void dtrip_schedule() {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-K fix-up shared by the tile families.  A workgroup is (tile, slice);
+// after its K slice, every slice stores its fp32 partial tile in lane order
+// (one contiguous 1 KiB per wave and store) and counts itself in; the slice
+// that arrives last sums all partials in slice order 0..splitk-1 -- the same
+// order whoever arrives last, so the result does not depend on timing -- and
+// resets the counter for the next launch.  Returns false in every other
+// slice, which then has nothing left to do; the last one returns true with
+// acc holding the total.
+//
+// The workgroups of one tile run on different XCDs, whose L2 caches are not
+// coherent with each other.  A device-scope fence would make that safe by
+// writing back and invalidating the whole L2 of the XCD, once per workgroup,
+// which costs the other workgroups their cached operand lines.  Instead only
+// the workspace traffic is made device-coherent: partials are stored and
+// loaded with device scope (cache policy SC1, which writes through and reads
+// past the XCD's L2), every wave waits until its stores are acknowledged
+// before the workgroup counts itself in, and the counter is a device-scope
+// atomic.  The last slice reads the partials only after its atomic returned.
+template <int FM, int FN, int NT, typename Acc>
+__device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs& p, int tile_id,
+                                             int slice, int splitk, int tid, int* s_last) {
+  constexpr int NACC = sizeof(Acc) / sizeof(float);
+  static_assert(NACC % 4 == 0, "accumulators come in float4 groups");
+  constexpr int NV = FM * FN * (NACC / 4);  // float4 values per lane
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const auto rsw = make_rsrc(reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT),
+                             (uint32_t)(splitk * NV * NT * 16));
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int g = 0; g < NACC / 4; ++g) {
+        const int v = (fm * FN + fn) * (NACC / 4) + g;
+        f4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsw,
+                                               (uint32_t)(((slice * NV + v) * NT + tid) * 16), 0,
+                                               kDeviceScope);
+      }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));  // vmcnt(0): partial stores acknowledged
+  __syncthreads();
+  if (tid == 0)
+    *s_last = __hip_atomic_fetch_add(&p.cnt[tile_id], 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == splitk - 1;
+  __syncthreads();
+  if (!*s_last) return false;
+  // running sum over slices 0..splitk-1 in order, VG float4 values per lane
+  // at a time; a slice's VG loads are issued together before any is added
+  constexpr int VG = NV < 16 ? NV : 16;
+  static_assert(NV % VG == 0, "whole groups");
+#pragma unroll
+  for (int v0 = 0; v0 < NV; v0 += VG) {
+    f4 sum[VG];
+#pragma unroll
+    for (int u = 0; u < VG; ++u) sum[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < splitk; ++s2) {
+      if (s2 == slice) {
+#pragma unroll
+        for (int u = 0; u < VG; ++u) {
+          const int v = v0 + u, fg = v / (NACC / 4), g = v % (NACC / 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum[u][e] += acc[fg / FN][fg % FN][4 * g + e];
+        }
+      } else {
+        f4 x[VG];
+#pragma unroll
+        for (int u = 0; u < VG; ++u)
+          x[u] = __builtin_bit_cast(
+              f4, __builtin_amdgcn_raw_buffer_load_b128(
+                      rsw, (uint32_t)(((s2 * NV + v0 + u) * NT + tid) * 16), 0, kDeviceScope));
+#pragma unroll
+        for (int u = 0; u < VG; ++u) sum[u] += x[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VG; ++u) {
+      const int v = v0 + u, fg = v / (NACC / 4), g = v % (NACC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[fg / FN][fg % FN][4 * g + e] = sum[u][e];
+    }
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.cnt[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // Split-K is compiled into the direct-to-LDS instances of at most 256 x 128
 // outputs: split-K pays only when output tiles are few, which larger tiles
 // make worse, and the fix-up's registers would spill in the 256 x 256 ones.
@@ -650,84 +739,7 @@ dtile_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));
 
   if (dtile_splits<BM, BN>() && splitk > 1) {
-    // Split-K fix-up.  Every slice stores its fp32 partial tile in lane order
-    // (one contiguous 1 KiB per wave and store) and counts itself in; the
-    // slice that arrives last sums all partials in slice order 0..splitk-1 --
-    // the same order whoever arrives last, so the result does not depend on
-    // timing -- writes C and resets the counter for the next launch.
-    //
-    // The workgroups of one tile run on different XCDs, whose L2 caches are
-    // not coherent with each other.  A device-scope fence would make that
-    // safe by writing back and invalidating the whole L2 of the XCD, once per
-    // workgroup, which costs the other workgroups their cached operand lines.
-    // Instead only the workspace traffic is made device-coherent: partials
-    // are stored and loaded with device scope (cache policy SC1, which writes
-    // through and reads past the XCD's L2), every wave waits until its stores
-    // are acknowledged before the workgroup counts itself in, and the
-    // counter is a device-scope atomic.  The last slice reads the partials
-    // only after its atomic has returned.
-    constexpr int NV = FM * FN * (MM::NACC / 4);  // float4 values per lane
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const auto rsw = make_rsrc(reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT),
-                               (uint32_t)(splitk * NV * NT * 16));
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int g = 0; g < MM::NACC / 4; ++g) {
-          const int v = (fm * FN + fn) * (MM::NACC / 4) + g;
-          f4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = acc[fm][fn][4 * g + e];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsw,
-                                                 (uint32_t)(((slice * NV + v) * NT + tid) * 16), 0,
-                                                 kDeviceScope);
-        }
-    __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));  // vmcnt(0): partial stores acknowledged
-    __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&p.cnt[tile_id], 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == splitk - 1;
-    __syncthreads();
-    if (!s_last) return;
-    // running sum over slices 0..splitk-1 in order, VG float4 values per lane
-    // at a time; a slice's VG loads are issued together before any is added
-    constexpr int VG = NV < 16 ? NV : 16;
-    static_assert(NV % VG == 0, "whole groups");
-#pragma unroll
-    for (int v0 = 0; v0 < NV; v0 += VG) {
-      f4 sum[VG];
-#pragma unroll
-      for (int u = 0; u < VG; ++u) sum[u] = f4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < splitk; ++s2) {
-        if (s2 == slice) {
-#pragma unroll
-          for (int u = 0; u < VG; ++u) {
-            const int v = v0 + u, fg = v / (MM::NACC / 4), g = v % (MM::NACC / 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum[u][e] += acc[fg / FN][fg % FN][4 * g + e];
-          }
-        } else {
-          f4 x[VG];
-#pragma unroll
-          for (int u = 0; u < VG; ++u)
-            x[u] = __builtin_bit_cast(
-                f4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rsw, (uint32_t)(((s2 * NV + v0 + u) * NT + tid) * 16), 0, kDeviceScope));
-#pragma unroll
-          for (int u = 0; u < VG; ++u) sum[u] += x[u];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < VG; ++u) {
-        const int v = v0 + u, fg = v / (MM::NACC / 4), g = v % (MM::NACC / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[fg / FN][fg % FN][4 * g + e] = sum[u][e];
-      }
-    }
-    if (tid == 0)
-      __hip_atomic_store(&p.cnt[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!splitk_fixup<FM, FN, NT>(acc, p, tile_id, slice, splitk, tid, &s_last)) return;
   }
 
   _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
@@ -881,6 +893,7 @@ d2tile_kernel(GemmArgs p) {
     constexpr int SPAN = NM;
     constexpr int nd = decltype(COPY)::value ? ND : 0;
     constexpr int nx = nd + NR;
+    constexpr int npair = nd < NR ? nd : NR;  // alternate while both kinds remain
     constexpr int sm = decltype(S_MFMA)::value, sr = decltype(S_READ)::value;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -890,11 +903,13 @@ d2tile_kernel(GemmArgs p) {
 #pragma unroll
       for (int x = 0; x < nx; ++x) {
         if (x * SPAN / nx != i) continue;
-        if (x < 2 * nd) {
+        if (x < 2 * npair) {
           if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
           else fread_one(rst, sr, x / 2);
+        } else if (nd > NR) {
+          dma_one(wst, kcopy, x - npair);
         } else {
-          fread_one(rst, sr, x - nd);
+          fread_one(rst, sr, x - npair);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -933,6 +948,229 @@ d2tile_kernel(GemmArgs p) {
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+
+  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+        h4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
+        buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                     (_Float16)acc[fm][fn][e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Deep-K direct-to-LDS family ("ktile"): BM x BN output tiles with a K step of
+// BK = 64*KB per trip (KB = 2 or 4), a ring of S LDS stages (S - 1 tiles of
+// copies in flight) and one barrier per trip.  Small tiles stay latency-bound
+// per trip, so a deep K step (few trips) is what makes them fast; the trip's
+// KSTEPS = 2*KB MFMA steps are pipelined as in d2tile: part j runs the MFMAs
+// of step j-1 while it reads the fragments of step j, and part 0 runs the last
+// step of the previous tile while it issues the copies of tile k+S-1.
+//
+// LDS rows hold one tile row's BK halves (128*KB bytes, 8*KB chunks of 16
+// bytes); logical chunk c of row r is stored at physical chunk c ^ (r & 15),
+// which measured free of bank conflicts for 16x16x32 fragment reads from
+// 256- and 512-byte rows.  A copy instruction fills a 1 KiB block of
+// RPB = 8/KB rows; lane l lands on row l / (8*KB) of the block, physical
+// chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+ktile_kernel(GemmArgs p) {
+  using MM = Mfma<16>;
+  constexpr int MF = 16, BK = 64 * KB, KSTEPS = 2 * KB;
+  constexpr int ROWH = BK;                 // halves per LDS row
+  constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
+  constexpr int RPB = 1024 / (2 * BK);     // rows per 1 KiB copy block
+  constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int A_BLK = BM / RPB / NW, B_BLK = BN / RPB / NW;  // copies per wave and trip
+  constexpr int ND = A_BLK + B_BLK;
+  constexpr int STAGE = (BM + BN) * ROWH;  // halves
+  static_assert(KB == 2 || KB == 4, "K step of 128 or 256");
+  static_assert(S == 2 || S == 3, "two or three LDS stages");
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BM % (RPB * NW) == 0 && BN % (RPB * NW) == 0, "copy blocks must split evenly");
+  static_assert(BM % 16 == 0, "B's rows start at a multiple of 16 LDS rows");
+  static_assert(S * STAGE * 2 <= 160 * 1024, "LDS budget");
+  static_assert(ND * (S - 2) < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[S * STAGE];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = p.M, N = p.N, K = p.K;
+  // split-K: workgroup id = tile * splitk + slice; slice s covers K range
+  // [s * kchunk, min(K, (s + 1) * kchunk)) (kchunk a multiple of 64)
+  const int splitk = p.splitk;
+  const int tile_id = blockIdx.x / splitk, slice = blockIdx.x - tile_id * splitk;
+  const int k_begin = splitk > 1 ? slice * p.kchunk : 0;
+  const int k_end = splitk > 1 ? min(K, k_begin + p.kchunk) : K;
+  int tm, tn;
+  tile_coords(tile_id, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  // per copy x of a trip: this lane's source offset (row and chunk) and the
+  // chunk's k offset within the trip
+  uint32_t c_off[ND];
+  int c_k[ND];
+#pragma unroll
+  for (int x = 0; x < ND; ++x) {
+    const bool is_a = x < A_BLK;
+    const int blk = is_a ? wave_u * A_BLK + x : wave_u * B_BLK + (x - A_BLK);
+    const int row = blk * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ (row & 15);
+    c_off[x] = (uint32_t)(row * (is_a ? lda : ldb) * 2 + c * 16);
+    c_k[x] = c * 8;
+  }
+  const bool mask_k = ((k_end - k_begin) % BK) != 0;
+  const uint32_t lds0 = lds_addr(lds);
+  // k0: the trip's first k (absolute); chunks at or past the slice's end read 0
+  auto dma_one = [&](int st, int k0, int x) {
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
+    const bool kin = !mask_k || (k0 + c_k[x] < k_end);
+    if (x < A_BLK) {
+      const int blk = wave_u * A_BLK + x;
+      dma16(rda, kin ? c_off[x] : kOOB, (uint32_t)k0 * 2, sbase + (uint32_t)(blk * 1024));
+    } else {
+      const int blk = wave_u * B_BLK + (x - A_BLK);
+      dma16(rdb, kin ? c_off[x] : kOOB, (uint32_t)k0 * 2,
+            sbase + (uint32_t)(BM * ROWH * 2 + blk * 1024));
+    }
+  };
+
+  // fragments of step s: the lane's row (a multiple of 16 plus lane % 16, so
+  // the swizzle term is lane % 16) at logical chunk 4*s + lane / 16
+  const int frow = lane % MF, fq = lane / MF;
+  int fa_off[KSTEPS], fb_off[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int phys = (4 * s + fq) ^ frow;
+    fa_off[s] = (wm * WTM + frow) * ROWH + phys * 8;
+    fb_off[s] = (BM + wn * WTN + frow) * ROWH + phys * 8;
+  }
+  h8 fa[2][FM], fb[2][FN];  // [step & 1]
+  auto fread_one = [&](int st, int s, int r) {
+    const _Float16* base = lds + st * STAGE;
+    if (r < FM)
+      fa[s & 1][r] = *reinterpret_cast<const h8*>(base + fa_off[s] + r * MF * ROWH);
+    else
+      fb[s & 1][r - FM] = *reinterpret_cast<const h8*>(base + fb_off[s] + (r - FM) * MF * ROWH);
+  };
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  constexpr int NM = FM * FN, NR = FM + FN;
+  // Part J of a trip: the NM MFMAs of step (J - 1) mod KSTEPS, with the NR
+  // fragment reads of step J -- and, in part 0, the copies of the tile S - 1
+  // ahead -- spread evenly over the MFMA slots (copies and reads alternate
+  // while copies last).
+  auto part = [&](auto JC, int rst, int kcopy, int wst) {
+    constexpr int J = decltype(JC)::value;
+    constexpr int sm = (J + KSTEPS - 1) % KSTEPS;
+    constexpr int nd = J == 0 ? ND : 0;
+    constexpr int nx = nd + NR;
+    constexpr int npair = nd < NR ? nd : NR;  // alternate while both kinds remain
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      const int fm = i / FN, fn = i % FN;
+      acc[fm][fn] = MM::mma(fb[sm & 1][fn], fa[sm & 1][fm], acc[fm][fn]);
+#pragma unroll
+      for (int x = 0; x < nx; ++x) {
+        if (x * NM / nx != i) continue;
+        if (x < 2 * npair) {
+          if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
+          else fread_one(rst, J, x / 2);
+        } else if (nd > NR) {
+          dma_one(wst, kcopy, x - npair);
+        } else {
+          fread_one(rst, J, x - npair);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // vmcnt(n) with the other counters left alone (gfx9 encoding)
+  auto wait_vm = [&](auto NC) {
+    constexpr int n = decltype(NC)::value;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  };
+  using WaitInFlight = std::integral_constant<int, ND * (S - 2)>;
+  using WaitAll = std::integral_constant<int, 0>;
+
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  // prologue: tiles 0 .. S-2 into stages 0 .. S-2, tile 0 published
+#pragma unroll
+  for (int t0 = 0; t0 < S - 1; ++t0)
+#pragma unroll
+    for (int x = 0; x < ND; ++x) dma_one(t0, k_begin + t0 * BK, x);
+  wait_vm(WaitInFlight{});
+  __syncthreads();
+  // trip 0's part 0 runs "the last step of tile -1" on zeroed fragments (adds 0)
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) fa[1][fm] = zero_h8();
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % S, wst = (kt + S - 1) % S;
+    const int kcopy = k_begin + (kt + S - 1) * BK;
+    part(std::integral_constant<int, 0>{}, st, kcopy, wst);
+    part(std::integral_constant<int, 1>{}, st, 0, 0);
+    part(std::integral_constant<int, 2>{}, st, 0, 0);
+    part(std::integral_constant<int, 3>{}, st, 0, 0);
+    if constexpr (KSTEPS == 8) {
+      part(std::integral_constant<int, 4>{}, st, 0, 0);
+      part(std::integral_constant<int, 5>{}, st, 0, 0);
+      part(std::integral_constant<int, 6>{}, st, 0, 0);
+      part(std::integral_constant<int, 7>{}, st, 0, 0);
+    }
+    wait_vm(WaitInFlight{});  // tile kt+1 has landed (later tiles may still be in flight)
+    __syncthreads();
+  }
+  // the last tile's last step (its fragments were read in the last trip)
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+  wait_vm(WaitAll{});  // copies of tiles past the end are drained before the workgroup exits
+  if (splitk > 1) {
+    if (!splitk_fixup<FM, FN, NT>(acc, p, tile_id, slice, splitk, tid, &s_last)) return;
+  }
 
   _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
@@ -1074,7 +1312,7 @@ generic_kernel(GemmArgs p) {
 // device-coherent fix-up as the direct-to-LDS family, slices summed in order)
 // fill the device while cutting that re-read.
 // Requires the 16-byte alignment class.
-template <int FM, int FN, int WAVES, int UNROLL>
+template <int FM, int FN, int WAVES, int UNROLL, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WAVES)
 skinny_kernel(GemmArgs p) {
   using MM = Mfma<16>;
@@ -1122,7 +1360,8 @@ skinny_kernel(GemmArgs p) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[fm][fn][v] = 0.0f;
 
-  h8 af[2][UNROLL][FM], bf[2][UNROLL][FN];
+  static_assert(DEPTH >= 2 && DEPTH <= 4, "2 to 4 register load groups");
+  h8 af[DEPTH][UNROLL][FM], bf[DEPTH][UNROLL][FN];
   auto load = [&](int buf, int s0) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
@@ -1146,16 +1385,22 @@ skinny_kernel(GemmArgs p) {
           acc[fm][fn] = MM::mma(bf[buf][u][fn], af[buf][u][fm], acc[fm][fn]);
   };
 
-  int g = wave;
-  if (g < ngroups) {
-    load(0, sl_lo + g * UNROLL);
-    for (; g + WAVES < ngroups; g += 2 * WAVES) {
-      load(1, sl_lo + (g + WAVES) * UNROLL);
-      compute(0);
-      load(0, sl_lo + (g + 2 * WAVES) * UNROLL);  // past the slice: every slot reads as 0
-      compute(1);
+  // DEPTH register groups: DEPTH - 1 groups of loads stay in flight while
+  // one is computed.  This wave's groups are j = 0, 1, ... (group index
+  // wave + j * WAVES); the count is rounded up to a multiple of DEPTH, and
+  // groups past the slice read as 0 and add nothing.
+  const int mine = wave < ngroups ? (ngroups - wave + WAVES - 1) / WAVES : 0;
+  auto grp = [&](int j) { return sl_lo + (wave + j * WAVES) * UNROLL; };
+  if (mine > 0) {
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) load(d, grp(d));
+    for (int j = 0; j < mine; j += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        load((d + DEPTH - 1) % DEPTH, grp(j + d + DEPTH - 1));
+        compute(d);
+      }
     }
-    if (g < ngroups) compute(0);
   }
 
   // partial tiles -> LDS, summed in wave order
@@ -1259,6 +1504,14 @@ hipError_t launch_dtile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+hipError_t launch_ktile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_d2tile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -1280,11 +1533,11 @@ int64_t grid_tile(int32_t M, int32_t N) {
   return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
 }
 
-template <int FM, int FN, int WAVES, int UNROLL>
+template <int FM, int FN, int WAVES, int UNROLL, int DEPTH = 2>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   const int64_t g =
       (int64_t)((a.M + 16 * FM - 1) / (16 * FM)) * ((a.N + 16 * FN - 1) / (16 * FN)) * a.splitk;
-  hipLaunchKernelGGL((skinny_kernel<FM, FN, WAVES, UNROLL>), dim3((unsigned)g), dim3(64 * WAVES),
+  hipLaunchKernelGGL((skinny_kernel<FM, FN, WAVES, UNROLL, DEPTH>), dim3((unsigned)g), dim3(64 * WAVES),
                      0, s, a);
   return hipGetLastError();
 }

@@ -32,10 +32,16 @@ def mangled(name):
         kind, bm, bn, wm, wn, mf, x = m.groups()
         return (f"_ZN4mihg12{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}ELi{x}"
                 "EEEvNS_8GemmArgsE")
-    m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)", name)
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)", name)
     if m:
-        fm, fn, w, u = m.groups()
-        return f"_ZN4mihg13skinny_kernelILi{fm}ELi{fn}ELi{w}ELi{u}EEEvNS_8GemmArgsE"
+        bm, bn, wm, wn, bk, s = m.groups()
+        return (f"_ZN4mihg12ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
+                "EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)(?:_d(\d+))?", name)
+    if m:
+        fm, fn, w, u, d = m.groups()
+        return (f"_ZN4mihg13skinny_kernelILi{fm}ELi{fn}ELi{w}ELi{u}ELi{d or 2}"
+                "EEEvNS_8GemmArgsE")
     raise AssertionError(f"unrecognised kernel name {name}")
 
 
