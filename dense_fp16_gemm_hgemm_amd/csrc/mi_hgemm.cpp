@@ -146,77 +146,59 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
   return sk;
 }
 
-// Built-in choice when the table has nothing close.  Small M streams B through
-// the skinny family; otherwise the largest LDS tile that still fills a good
-// part of the machine ([P2] 正文 paragraph 3: large tiles raise reuse and
-// lower occupancy).  The thresholds come from timing every instance on
-// MI355X over the LLM projection and square shapes: one partial wave of
-// 256x256 tiles beats more waves of smaller tiles down to half a wave
-// (the chip is power-bound, so idle CUs buy clock for the busy ones), and
-// when even 128x128 tiles leave half the CUs idle, splitting K over them
-// beats smaller tiles once K is long.
+// Built-in choice when the table has nothing close: the largest tile that
+// still fills a good part of the machine ([P2] 正文 paragraph 3: large tiles
+// raise reuse and lower occupancy), else a K split.  The thresholds come from
+// timing every instance over the LLM projection and square shapes on MI355X:
+//  - one partial wave of 256x256 tiles beats more waves of smaller tiles down
+//    to half a wave (the chip is power-bound: idle CUs buy clock for the busy
+//    ones);
+//  - below that, the deep-K tiles (K step 128) win: 128x128, then 64x64, then
+//    32x64 / 16x64 for the smallest M; small tiles are latency-bound per K
+//    step, so a deep step beats more parallel tiles;
+//  - when even those leave half the CUs idle and K is long, K is split.
 Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
   Config c;
   if (!aligned) return c;
-  const int k128 = find_kernel("dtile_128x128_w2x2_m16_s4");
-  const int64_t t128 = k128 >= 0 ? kKernels[k128].grid((int32_t)M, (int32_t)N) : 0;
-  // as many K slices of 128x128 tiles as keep every slice >= 1024 deep and
-  // the grid <= 256 workgroups (1 = no split)
-  auto split_for = [&]() {
+  auto tiles = [&](int k) { return k >= 0 ? kKernels[k].grid((int32_t)M, (int32_t)N) : 0; };
+  // as many K slices of kernel k as keep every slice >= 1024 deep and the
+  // grid <= 256 workgroups (1 = no split)
+  auto split_for = [&](int k) {
+    if (k < 0 || !kKernels[k].splitk_ok) return 1;
+    const int64_t t = tiles(k);
     int s = 1;
-    while (s < 8 && t128 * s * 2 <= 256 && K / (s * 2) >= 1024) s *= 2;
+    while (s < 8 && t * s * 2 <= 256 && K / (s * 2) >= 1024) s *= 2;
     int64_t chunk = K;
-    return (s > 1 && effective_split(kKernels[k128], M, N, K, s, &chunk) > 1) ? s : 1;
+    return (s > 1 && effective_split(kKernels[k], M, N, K, s, &chunk) > 1) ? s : 1;
   };
-  if (M <= 64) {
-    // M <= 32: stream B through the skinny family (wider column tiles when N
-    // is large).  M <= 64 with N or K of 8192 and more: split K over 128x128
-    // tiles, whose MFMAs then do the work; otherwise skinny.
-    if (M > 32 && k128 >= 0 && (N >= 8192 || K >= 8192) && K >= 2048) {
-      const int s = split_for();
-      if (s > 1) {
-        c.kernel = k128;
-        c.splitk = s;
-        return c;
-      }
-    }
-    const char* name = M <= 16 ? (N >= 8192 ? "skinny_1x4_w4_u2" : "skinny_1x1_w4_u4")
-                       : M <= 32 ? "skinny_2x1_w8_u4" : "skinny_2x2_w4_u4";
-    c.kernel = find_kernel(name);
-    if (c.kernel < 0) c.kernel = kGenericKernel;
-    return c;
-  }
-  const int k256 = find_kernel("d2tile_256x256_w2x4_m16");
-  const int64_t t256 = k256 >= 0 ? kKernels[k256].grid((int32_t)M, (int32_t)N) : 0;
-  if (k256 >= 0 && t256 >= 128) {
-    c.kernel = k256;
-    c.group_m = 8;
-    c.xcd = 1;
-    return c;
-  }
-  if (k128 >= 0 && t128 >= 128) {
-    c.kernel = k128;
-    c.group_m = 4;
-    c.xcd = 1;
-    return c;
-  }
-  if (k128 >= 0 && K >= 2048) {
-    const int s = split_for();
-    if (s > 1) {
-      c.kernel = k128;
-      c.splitk = s;
-      return c;
-    }
-  }
-  static const char* const small[] = {"tile_128x64_w2x2_m32", "tile_64x64_w2x2_m32"};
-  for (const char* name : small) {
-    const int k = find_kernel(name);
-    if (k < 0) continue;
+  auto pick = [&](int k, int g, int x, int s) {
     c.kernel = k;
-    c.group_m = 8;
-    c.xcd = 1;
-    if (kKernels[k].grid((int32_t)M, (int32_t)N) >= 256) break;
+    c.group_m = g;
+    c.xcd = x;
+    c.splitk = s;
+  };
+  const int k256 = find_kernel("d2tile_256x256_w2x4_m16");
+  const int k128 = find_kernel("ktile_128x128_w2x2_k128_s2");
+  const int k64 = find_kernel("ktile_64x64_w2x2_k128_s3");
+  const int k32 = find_kernel("ktile_32x64_w2x2_k128_s3");
+  const int k16 = find_kernel("ktile_16x64_w1x4_k128_s3");
+  if (M > 64 && k256 >= 0 && tiles(k256) >= 128) {
+    pick(k256, 8, 1, 1);
+  } else if (M > 64 && k128 >= 0 && tiles(k128) >= 128) {
+    pick(k128, 8, 1, split_for(k128));
+  } else if (M > 32 && k64 >= 0 && (tiles(k64) >= 128 || K >= 8192)) {
+    const int s = split_for(k64);
+    pick(k64, s > 1 ? 1 : 8, s > 1 ? 0 : 1, s);
+  } else if (M > 16 && k32 >= 0) {
+    pick(k32, 1, 0, split_for(k32));
+  } else if (k16 >= 0 && (tiles(k16) >= 128 || K >= 8192)) {
+    pick(k16, 1, 0, split_for(k16));
+  } else {
+    // 16 rows or fewer over a short K: B streamed straight into registers
+    const int ks = find_kernel("skinny_1x1_w4_u4");
+    pick(ks >= 0 ? ks : kGenericKernel, 1, 0, 1);
   }
+  if (c.kernel < 0) c.kernel = kGenericKernel;
   return c;
 }
 

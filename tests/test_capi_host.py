@@ -141,25 +141,30 @@ def test_misalignment_selects_the_elementwise_instance(inspect_handle):
 def test_heuristic_picks_by_shape(inspect_handle):
     h = inspect_handle
     names = mh.kernel_names()
-    assert names[plan(h, 16, 4096, 4096)[1]].startswith("skinny_")
-    assert names[plan(h, 8192, 8192, 8192)[1]] == "d2tile_256x256_w2x4_m16"
-    small = names[plan(h, 256, 256, 256)[1]]
-    assert "tile_" in small and small != "d2tile_256x256_w2x4_m16"
-    r = plan(h, 256, 4096, 4096)                     # 16 large tiles: split K over 128x128 tiles
-    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 4
+
+    def choice(M, N, K):
+        r = plan(h, M, N, K)
+        assert r[0] == mh.MI_HGEMM_OK
+        return names[r[1]], r[4]
+
     # half a wave or more of 256x256 tiles keeps the large tile
-    assert names[plan(h, 1024, 14336, 4096)[1]] == "d2tile_256x256_w2x4_m16"
-    # fewer: 128x128 tiles while there are 128 of them, unsplit
-    r = plan(h, 256, 11008, 4096)
-    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 1
-    # M = 64: split K for wide or deep shapes, skinny otherwise
-    r = plan(h, 64, 11008, 4096)
-    assert names[r[1]] == "dtile_128x128_w2x2_m16_s4" and r[4] == 2
-    assert names[plan(h, 64, 4096, 4096)[1]] == "skinny_2x2_w4_u4"
-    assert names[plan(h, 16, 14336, 4096)[1]] == "skinny_1x4_w4_u2"
-    # short K: no split, small tiles fill the machine instead
-    r = plan(h, 256, 4096, 1024)
-    assert r[4] == 1 and names[r[1]] == "tile_64x64_w2x2_m32"
+    assert choice(8192, 8192, 8192) == ("d2tile_256x256_w2x4_m16", 1)
+    assert choice(1024, 14336, 4096) == ("d2tile_256x256_w2x4_m16", 1)
+    # then deep-K 128x128 tiles while there are 128 of them
+    assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x2_k128_s2", 1)
+    assert choice(256, 11008, 4096) == ("ktile_128x128_w2x2_k128_s2", 1)
+    # then 64x64, split over K when the tiles are few and K is long
+    assert choice(256, 4096, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
+    assert choice(64, 11008, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
+    assert choice(64, 4096, 11008) == ("ktile_64x64_w2x2_k128_s3", 4)
+    # M <= 64 over a short K: 32x64 tiles, split to fill the device
+    assert choice(64, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3", 2)
+    # 16 rows: 16x64 deep-K tiles for wide or deep shapes, skinny otherwise
+    assert choice(16, 14336, 4096) == ("ktile_16x64_w1x4_k128_s3", 1)
+    assert choice(16, 4096, 11008) == ("ktile_16x64_w1x4_k128_s3", 4)
+    assert choice(16, 4096, 4096) == ("skinny_1x1_w4_u4", 1)
+    # a short K is never split
+    assert choice(256, 4096, 1024)[1] == 1
 
 
 def test_nearest_table_entry_drops_a_split_that_does_not_fit(tmp_path, monkeypatch):
