@@ -61,18 +61,23 @@ def parse():
     return ap.parse_args()
 
 
+# the device code of the kernels (host dispatch code and tables are not part of it)
+DEVICE_SOURCES = ("kernels.hpp", "instances.hip", "internal.h")
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in DEVICE_SOURCES:
+        with open(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
+def load_traffic(kernel: str, workload: str, group_m: int, xcd_remap: int, split_k: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when there is none or it was taken on other kernel sources."""
+    when there is none, it was taken on other kernel sources, or with another
+    raster or K split (both change the traffic)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -85,6 +90,9 @@ def load_traffic(kernel: str, workload: str):
     if vals.get("source_digest") != source_digest():
         return None
     try:
+        if (int(vals["group_m"]), int(vals["xcd_remap"]), int(vals["split_k"])) != \
+                (group_m, xcd_remap, split_k):
+            return None
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
@@ -165,7 +173,7 @@ def time_steps(run, wl, steps, warmup):
     return total_ms / steps, statistics.fmean(per), wall, per
 
 
-def roofline(p, launch_ms, kernel, workload):
+def roofline(p, launch_ms, kernel, workload, raster=(1, 0, 1)):
     flops, nbytes = p.flops, p.min_bytes
     t = launch_ms * 1e-3
     ai = flops / nbytes
@@ -175,7 +183,7 @@ def roofline(p, launch_ms, kernel, workload):
     else:
         achieved, peak, unit, bound = nbytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel, workload),
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(kernel, workload, *raster),
             "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
 
 
@@ -276,7 +284,7 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
            "ms_per_step": ms, "us_per_call": round(launch_ms * 1e3, 3),
            "us_per_call_median": round(statistics.median(per) * 1e3, 3),
            "tflops": round(p.flops / (ms * 1e-3) / 1e12, 3), "wall_s": wall,
-           "roofline": roofline(p, launch_ms, kernel, p.name)}
+           "roofline": roofline(p, launch_ms, kernel, p.name, (gm, xcd, sk))}
     if with_torch:
         rec["torch_matmul_tflops"], rec["torch_matmul_us"] = torch_matmul_context(wl)
     if device_time:
@@ -286,7 +294,7 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
         dus = graph_us(run, wl, reps)
         rec["device_us_per_call"] = round(dus, 3)
         rec["device_tflops"] = round(p.flops / (dus * 1e-6) / 1e12, 3)
-        rec["device_roofline"] = roofline(p, dus * 1e-3, kernel, p.name)
+        rec["device_roofline"] = roofline(p, dus * 1e-3, kernel, p.name, (gm, xcd, sk))
         if with_torch:
             import torch
 

@@ -567,8 +567,25 @@ struct TimingStream {
 
 // Capture `reps` launches of one candidate on stream `ts` into a graph and
 // time 5 replays; appends microseconds per launch to `trials`.
+// The timing operands: nsets copies of (A, B) back to back, set i at
+// base + i * (M + N) * K halves (A first).
+struct TimingSets {
+  _Float16* base = nullptr;
+  int nsets = 1;
+  const void* A(int64_t M, int64_t N, int64_t K, int i) const {
+    return base + (int64_t)i * (M + N) * K;
+  }
+  const void* B(int64_t M, int64_t N, int64_t K, int i) const {
+    return base + (int64_t)i * (M + N) * K + M * K;
+  }
+};
+
+// Capture `reps` launches of one candidate on stream `ts` into a graph (launch r
+// reads timing set r mod nsets, so that together they overflow the MALL and
+// each launch reads its operands from HBM, as in real use) and time 5 replays;
+// appends microseconds per launch to `trials`.
 hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t N, int64_t K,
-                        const void* A, const void* B, void* C, int64_t ldc, int reps,
+                        const TimingSets& sets, void* C, int64_t ldc, int reps,
                         hipStream_t ts, hipEvent_t ev0, hipEvent_t ev1,
                         std::vector<double>& trials) {
   hipGraph_t graph = nullptr;
@@ -577,7 +594,8 @@ hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t 
   if (e != hipSuccess) return e;
   mi_hgemm_status_t st = MI_HGEMM_OK;
   for (int r = 0; r < reps && st == MI_HGEMM_OK; ++r)
-    st = launch(h, cand, M, N, K, A, K, B, K, C, ldc, ts);
+    st = launch(h, cand, M, N, K, sets.A(M, N, K, r % sets.nsets), K, sets.B(M, N, K, r % sets.nsets),
+                K, C, ldc, ts);
   e = hipStreamEndCapture(ts, &graph);
   if (e == hipSuccess && st != MI_HGEMM_OK) e = hipErrorLaunchFailure;
   if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -615,22 +633,30 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t ldc = (N + 7) / 8 * 8;
 
-  // a, b: small integers, for the bit-exact check; ta, tb: random mantissas
-  // scaled by 1/sqrt(K), for timing (the clock depends on the data)
-  Scratch a, b, ta, tb, c, cref, cnt;
+  // a, b: small integers, for the bit-exact check.  Timing sets: random
+  // mantissas scaled by 1/sqrt(K) (the clock depends on the data), in as many
+  // copies as make 2.2x the 256 MiB MALL (at most 64 copies and 4 GiB), so
+  // that the timed launches read their operands from HBM.
+  Scratch a, b, tsets, c, cref, cnt;
   hipError_t e;
+  const double set_bytes = (double)(M + N) * K * 2;
+  TimingSets sets;
+  sets.nsets = (int)std::max(1.0, std::min({64.0, std::ceil(2.2 * 256.0 * 1048576.0 / set_bytes),
+                                            std::floor(4.0 * 1073741824.0 / set_bytes)}));
   if ((e = hipMalloc(&a.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&b.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
-  if ((e = hipMalloc(&ta.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
-  if ((e = hipMalloc(&tb.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&tsets.p, (size_t)sets.nsets * (M + N) * K * 2)) != hipSuccess)
+    return hip_fail(h, e);
+  sets.base = static_cast<_Float16*>(tsets.p);
   if ((e = hipMalloc(&c.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cref.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cnt.p, sizeof(int))) != hipSuccess) return hip_fail(h, e);
   if ((e = mihg::launch_fill_small_int(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
   if ((e = mihg::launch_fill_small_int(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
   const float tscale = 1.0f / std::sqrt((float)K);
-  if ((e = mihg::launch_fill_uniform(ta.p, M * K, 0x9abcu, tscale, s)) != hipSuccess) return hip_fail(h, e);
-  if ((e = mihg::launch_fill_uniform(tb.p, N * K, 0xdef0u, tscale, s)) != hipSuccess) return hip_fail(h, e);
+  if ((e = mihg::launch_fill_uniform(tsets.p, (int64_t)sets.nsets * (M + N) * K, 0x9abcu, tscale,
+                                     s)) != hipSuccess)
+    return hip_fail(h, e);
 
   // Reference result: the element-wise instance.
   Config ref;
@@ -724,16 +750,18 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     // than host launch cost; the median of 5 replays is kept
     float ms = 0.f;
     (void)hipEventRecord(ev0, s);
-    (void)launch(h, cand, M, N, K, ta.p, K, tb.p, K, c.p, ldc, s);
+    (void)launch(h, cand, M, N, K, sets.A(M, N, K, 0), K, sets.B(M, N, K, 0), K, c.p, ldc, s);
     (void)hipEventRecord(ev1, s);
     if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
       result = hip_fail(h, e);
       break;
     }
     (void)hipEventElapsedTime(&ms, ev0, ev1);
-    const int reps = (int)std::min(200.0, std::max(1.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
+    // about 1 ms of launches, and every timing set at least once
+    const int reps = (int)std::max((double)sets.nsets,
+                                   std::min(200.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
     std::vector<double> trials;
-    e = time_replays(h, cand, M, N, K, ta.p, tb.p, c.p, ldc, reps, ts.s, ev0, ev1, trials);
+    e = time_replays(h, cand, M, N, K, sets, c.p, ldc, reps, ts.s, ev0, ev1, trials);
     if (e != hipSuccess) {
       result = hip_fail(h, e);
       break;

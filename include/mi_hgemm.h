@@ -120,9 +120,11 @@ mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_
  * discarded); it is then timed on operands with random mantissas scaled by
  * 1/sqrt(K) (the clock under load depends on the data), as the median of 5
  * replays of a captured graph of repeated launches on a private stream.  The
- * fastest correct one becomes the handle's entry for the shape.
+ * launches rotate over enough operand copies to overflow the 256 MiB MALL
+ * (at most 64 copies and 4 GiB), so each reads its operands from HBM as in
+ * real use.  The fastest correct one becomes the handle's entry for the shape.
  * With MI_HGEMM_TUNE_PERSIST the entry is appended to the handle's table file.
- * Synchronises `stream`.  Allocates scratch (two operand sets and two
+ * Synchronises `stream`.  Allocates scratch (the operand sets and two
  * outputs, freed before returning).
  * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
  */
