@@ -17,11 +17,10 @@ namespace mihg {
 // the device code object holds every kernel) and into the registry (host pass).
 //   TILE:   X(BM, BN, WGM, WGN, MF)
 //   SKINNY: X(FM, FN, WAVES, UNROLL)
+// (256 x 256 register-staged tiles with 16x16 MFMAs, or with 4 waves, spill;
+// the direct-to-LDS families cover that size.)
 #define MIHG_TILE_INSTANCES(X) \
-  X(256, 256, 2, 2, 32)          \
   X(256, 256, 2, 4, 32)          \
-  X(256, 256, 2, 2, 16)          \
-  X(256, 256, 2, 4, 16)          \
   X(128, 128, 2, 2, 16)          \
   X(256, 128, 2, 2, 32)          \
   X(128, 256, 2, 2, 32)          \
@@ -51,6 +50,11 @@ namespace mihg {
   X(128, 64, 2, 2)                \
   X(64, 128, 2, 2)                \
   X(64, 64, 2, 2)
+
+// PPTILE: X(BM, BN): eight waves in two ping-pong groups
+#define MIHG_PPTILE_INSTANCES(X) \
+  X(256, 256)                    \
+  X(256, 128)
 
 // KTILE: X(BM, BN, WGM, WGN, BK, S): K step BK (128 or 256), S LDS stages
 #define MIHG_KTILE_INSTANCES(X) \
@@ -91,6 +95,7 @@ namespace mihg {
   template __global__ void dtile_kernel<BM, BN, WGM, WGN, MF, S>(GemmArgs);
 #define INSTANTIATE_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
 #define INSTANTIATE_SKINNY(FM, FN, W, U) \
@@ -99,6 +104,7 @@ template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
 MIHG_TILE_INSTANCES(INSTANTIATE_TILE)
 MIHG_DTILE_INSTANCES(INSTANTIATE_DTILE)
 MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
+MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 
@@ -115,6 +121,9 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
    1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+#define PPTILE_DESC(BM, BN)                                                                \
+  {"pptile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                     \
+   2 * (BM + BN) * kD2Row * 2, 0, &launch_pptile<BM, BN>, &grid_tile<BM, BN>},
 #define KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1, &launch_ktile<BM, BN, WGM, WGN, BK / 64, S>, \
@@ -130,6 +139,7 @@ const KernelDesc kKernels[] = {
     MIHG_TILE_INSTANCES(TILE_DESC)
     MIHG_DTILE_INSTANCES(DTILE_DESC)
     MIHG_D2TILE_INSTANCES(D2TILE_DESC)
+    MIHG_PPTILE_INSTANCES(PPTILE_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
 };

@@ -981,6 +981,207 @@ d2tile_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong family ("pptile"): BM x BN x 64 tiles, 8 waves in two groups of
+// four that take turns at the matrix pipes.  Group g owns tile rows
+// [g*BM/2, (g+1)*BM/2); its four waves hold (BM/4) x (BN/2) each.  Time is cut
+// into slots, each ended by one workgroup barrier; in every slot one group
+// runs the MFMAs of one 32-deep K step (at raised wave priority) while the
+// other reads the next step's fragments from LDS into registers, so each
+// SIMD has one wave feeding its matrix pipe and one doing memory work.  Each
+// wave runs the same read / multiply / read / multiply loop, group 1 one
+// slot behind group 0, so for K tile t (steps 0 and 1):
+//   slot 4t+1: group 0 copies tile t+1 (global -> LDS), reads step 0 of t;
+//              group 1 multiplies step 1 of tile t-1
+//   slot 4t+2: group 0 multiplies step 0;  group 1 reads step 0
+//   slot 4t+3: group 0 reads step 1;       group 1 multiplies step 0
+//   slot 4t+4: group 0 multiplies step 1 and waits for its copies of t+1;
+//              group 1 reads step 1
+// Only group 0 copies; it overwrites a stage (slot 4t+1) only after group 1's
+// last read of it (slot 4t), and its copies have landed (end of slot 4t+4)
+// before anyone reads them (slot 4t+5).  One step's fragments (48 registers
+// at 256 x 256) sit beside 128 accumulators within the 256 registers of a
+// wave that shares its SIMD.  LDS layout and copies as in d2tile (128-byte
+// rows, chunk XOR (row >> 1) & 7, two LDS stages).
+template <int BM, int BN>
+__global__ void __launch_bounds__(512)
+pptile_kernel(GemmArgs p) {
+  using MM = Mfma<16>;
+  constexpr int MF = 16, BK = 64, KSTEPS = 2;
+  constexpr int WTM = BM / 4, WTN = BN / 2;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int A_BLK = BM / 8 / 4, B_BLK = BN / 8 / 4;  // 1 KiB copies per group-0 wave
+  constexpr int ND = A_BLK + B_BLK;
+  constexpr int STAGE = (BM + BN) * kD2Row;
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "copy blocks pair up by parity");
+
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int wm = w4 >> 1, wn = w4 & 1;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+  // copies (group 0): lane l -> row l/8 of an 8-row block, physical chunk
+  // l%8, which holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
+  const int drow = lane >> 3;
+  const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const uint32_t a_v0 = (uint32_t)(drow * lda * 2 + dch0 * 16), a_v1 = (uint32_t)(drow * lda * 2 + dch1 * 16);
+  const uint32_t b_v0 = (uint32_t)(drow * ldb * 2 + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * 2 + dch1 * 16);
+  const bool mask_k = (K & 63) != 0;
+  const uint32_t lds0 = lds_addr(lds);
+  auto dma_one = [&](int st, int k0, int x) {
+    const uint32_t kb = (uint32_t)k0 * 2;
+    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
+    if (x < A_BLK) {
+      const int blk = w4 * A_BLK + x;
+      const int ch = (x & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (k0 + ch * 8 < K);
+      dma16(rda, kin ? ((x & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
+            sbase + blk * 8 * kD2Row * 2);
+    } else {
+      const int xb = x - A_BLK;
+      const int blk = w4 * B_BLK + xb;
+      const int ch = (xb & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (k0 + ch * 8 < K);
+      dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
+            sbase + (BM + blk * 8) * kD2Row * 2);
+    }
+  };
+
+  // fragments: this wave's rows (group half, wave row) at logical chunk 4s + l/16
+  const int frow = lane % MF, fq = lane / MF, fsw = (frow >> 1) & 7;
+  int fa_off[KSTEPS], fb_off[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int phys = (4 * s + fq) ^ fsw;
+    fa_off[s] = (grp * (BM / 2) + wm * WTM + frow) * kD2Row + phys * 8;
+    fb_off[s] = (BM + wn * WTN + frow) * kD2Row + phys * 8;
+  }
+  h8 fa[FM], fb[FN];  // one step's fragments
+  auto fread_one = [&](int st, int s, int r) {  // read r of step s: A then B
+    const _Float16* base = lds + st * STAGE;
+    if (r < FM)
+      fa[r] = *reinterpret_cast<const h8*>(base + fa_off[s] + r * MF * kD2Row);
+    else
+      fb[r - FM] = *reinterpret_cast<const h8*>(base + fb_off[s] + (r - FM) * MF * kD2Row);
+  };
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+
+  constexpr int NR = FM + FN;
+  constexpr int npair = ND < NR ? ND : NR;
+  // memory slot: step s's NR fragment reads from stage rst, with (group 0,
+  // step 0) the ND copies of the next tile into stage wst; copies and reads
+  // alternate while both last
+  auto mem = [&](auto S, bool copy, int rst, int kcopy, int wst) {
+    constexpr int s = decltype(S)::value;
+    if (copy) {
+#pragma unroll
+      for (int x = 0; x < NR + ND; ++x) {
+        if (x < 2 * npair) {
+          if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
+          else fread_one(rst, s, x / 2);
+        } else if (ND > NR) {
+          dma_one(wst, kcopy, x - npair);
+        } else {
+          fread_one(rst, s, x - npair);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) fread_one(rst, s, r);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // MFMA slot: one step's MFMAs, at raised priority
+  auto mfma = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[fn], fa[fm], acc[fm][fn]);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto wait_all = [&]() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8)); };  // vmcnt(0)
+
+  const int nk = (K + BK - 1) / BK;
+  // prologue: group 0 copies tile 0 into stage 0
+  if (grp == 0) {
+#pragma unroll
+    for (int x = 0; x < ND; ++x) dma_one(0, 0, x);
+    wait_all();
+  }
+  __syncthreads();
+  // Both groups run the same four-slot loop; group 1 starts one barrier late,
+  // which puts it one slot behind group 0 for the whole loop, and group 0
+  // ends with one extra barrier so that both pass the same number.
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  const bool copier = grp == 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    mem(S0{}, copier && kt + 1 < nk, st, (kt + 1) * BK, st ^ 1);
+    __syncthreads();
+    mfma();
+    __syncthreads();
+    mem(S1{}, false, st, 0, 0);
+    __syncthreads();
+    mfma();
+    wait_all();  // group 0: its copies of tile kt+1 have landed
+    __syncthreads();
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+
+  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = grp * (BM / 2) + wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+        h4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
+        buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = grp * (BM / 2) + wm * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                     (_Float16)acc[fm][fn][e]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Deep-K direct-to-LDS family ("ktile"): BM x BN output tiles with a K step of
 // BK = 64*KB per trip (KB = 2 or 4), a ring of S LDS stages (S - 1 tiles of
 // copies in flight) and one barrier per trip.  Small tiles stay latency-bound
@@ -1501,6 +1702,13 @@ hipError_t launch_dtile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * sk;
   hipLaunchKernelGGL((dtile_kernel<BM, BN, WGM, WGN, MF, S>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_pptile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((pptile_kernel<BM, BN>), dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -27,6 +27,10 @@ def mangled(name):
     if m:
         bm, bn, wm, wn = m.groups()
         return f"_ZN4mihg13d2tile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"pptile_(\d+)x(\d+)_w8_m16", name)
+    if m:
+        bm, bn = m.groups()
+        return f"_ZN4mihg13pptile_kernelILi{bm}ELi{bn}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"(dtile)_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)_(?:la|s)(\d+)", name)
     if m:
         kind, bm, bn, wm, wn, mf, x = m.groups()
@@ -64,3 +68,34 @@ def test_every_registered_kernel_has_gfx950_code(tmp_path):
     have = set(re.findall(r"(_ZN4mihg\S+)", syms))
     missing = [n for n in mh.kernel_names() if mangled(n) not in have]
     assert not missing, f"kernels without device code: {missing}"
+
+
+@pytest.mark.skipif(not (shutil.which("objcopy") and os.path.exists(LLVM + "/llvm-readelf")),
+                    reason="binutils / ROCm llvm tools not available")
+def test_no_registered_kernel_spills_to_scratch(tmp_path):
+    """Register spills go to per-lane scratch memory and wreck a tile's schedule."""
+    fat = tmp_path / "fat.bin"
+    subprocess.run(["objcopy", "--dump-section", f".hip_fatbin={fat}", mh.LIB_PATH,
+                    str(tmp_path / "copy.so")], check=True)
+    targets = subprocess.run([LLVM + "/clang-offload-bundler", "--list", "--type=o",
+                              f"--input={fat}"], check=True, capture_output=True,
+                             text=True).stdout.split()
+    gfx = [t for t in targets if t.endswith("gfx950")]
+    co = tmp_path / "dev.co"
+    subprocess.run([LLVM + "/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    f"--targets={gfx[0]}", f"--output={co}"], check=True)
+    notes = subprocess.run([LLVM + "/llvm-readelf", "--notes", "-W", str(co)], check=True,
+                           capture_output=True, text=True).stdout
+    info = {}
+    for block in re.split(r"\n\s*- \.", notes):
+        name = re.search(r"\.name:\s+(\S+)", "." + block)
+        if not name:
+            continue
+        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
+        priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
+        info[name.group(1)] = (int(spill.group(1)) if spill else 0,
+                               int(priv.group(1)) if priv else 0)
+    wanted = {mangled(n): n for n in mh.kernel_names()}
+    assert set(wanted) <= set(info), "metadata missing for some kernels"
+    bad = {wanted[m]: info[m] for m in wanted if info[m] != (0, 0)}
+    assert not bad, f"kernels with spills or private segment (spills, bytes): {bad}"
