@@ -12,6 +12,10 @@ gcc and marshals numpy arrays through ctypes.  The operation follows
 B ("TN").  With B column-major K x N, its storage is N rows of K halves, i.e. the
 ``Bt`` array below, and ``C = A @ Bt.T``.
 
+``igemm_tn`` is the int8 variant: the exact integer sum of int8 products,
+stored as int32 (the INT8 mode of the same page's 正文 paragraph 3; the page
+leaves the result type open and the exact int32 sum is the reading taken).
+
 Parity pins for every function here live in ``tests/test_oracle_pins.py``; no
 function of the oracle is unpinned.
 """
@@ -46,19 +50,20 @@ def build(force: bool = False) -> str:
     return LIB_PATH
 
 
-def _as_rows(x: np.ndarray, name: str) -> tuple[np.ndarray, int]:
-    """(array, leading dimension in elements) for a 2-D float16 array whose rows
-    may be padded (row stride >= row length) but whose elements are unit-stride."""
+def _as_rows(x: np.ndarray, name: str, dtype=np.float16) -> tuple[np.ndarray, int]:
+    """(array, leading dimension in elements) for a 2-D array of ``dtype`` whose
+    rows may be padded (row stride >= row length) but whose elements are unit-stride."""
     if x.ndim != 2:
         raise ValueError(f"{name} must be 2-D")
-    if x.dtype != np.float16:
-        raise TypeError(f"{name} must be float16, got {x.dtype}")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {np.dtype(dtype).name}, got {x.dtype}")
+    es = x.itemsize
     rows, cols = x.shape
     if rows <= 1:
         return x if x.flags.c_contiguous else np.ascontiguousarray(x), max(cols, 1)
-    if (cols > 1 and x.strides[1] != 2) or x.strides[0] % 2 or x.strides[0] // 2 < cols:
+    if (cols > 1 and x.strides[1] != es) or x.strides[0] % es or x.strides[0] // es < cols:
         x = np.ascontiguousarray(x)
-    return x, int(x.strides[0] // 2)
+    return x, int(x.strides[0] // es)
 
 
 class Oracle:
@@ -80,6 +85,10 @@ class Oracle:
         lib.ref_hgemm_tn_entries.restype = ctypes.c_int
         lib.ref_hgemm_tn_entries.argtypes = [i64, i64, i64, p, i64, p, i64,
                                              i64, p, p, p, p]
+        lib.ref_igemm_tn.restype = ctypes.c_int
+        lib.ref_igemm_tn.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+        lib.ref_igemm_tn_entries.restype = ctypes.c_int
+        lib.ref_igemm_tn_entries.argtypes = [i64, i64, i64, p, i64, p, i64, i64, p, p, p]
         lib.ref_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -152,6 +161,58 @@ class Oracle:
         vals = out.view(np.float16)
         return (vals, sums) if return_sums else vals
 
+    def igemm_tn(self, A: np.ndarray, Bt: np.ndarray,
+                 C: np.ndarray | None = None) -> np.ndarray:
+        """C[M,N] = A[M,K] @ Bt[N,K].T for int8 operands, exact, as int32.
+
+        Raises OverflowError when a sum does not fit int32.  A given ``C``
+        (int32, unit-stride rows, possibly a padded view) is written in place.
+        """
+        A, lda = _as_rows(A, "A", np.int8)
+        Bt, ldb = _as_rows(Bt, "Bt", np.int8)
+        M, K = A.shape
+        N, K2 = Bt.shape
+        if K != K2:
+            raise ValueError(f"K mismatch: A has {K}, Bt has {K2}")
+        if C is None:
+            C = np.empty((M, N), dtype=np.int32)
+        if M == 0 or N == 0:
+            if C.shape != (M, N):
+                raise ValueError("C must have shape (M, N)")
+            return C
+        if C.shape != (M, N) or C.dtype != np.int32 or (N > 1 and C.strides[1] != 4):
+            raise ValueError("C must be an int32 (M, N) array with unit-stride rows")
+        ldc = C.strides[0] // 4 if M > 1 else max(N, 1)
+        rc = self.lib.ref_igemm_tn(M, N, K, A.ctypes.data, lda, Bt.ctypes.data, ldb,
+                                   C.ctypes.data, ldc)
+        if rc == -2:
+            raise OverflowError("an int8 dot product does not fit int32")
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return C
+
+    def igemm_tn_entries(self, A: np.ndarray, Bt: np.ndarray, rows, cols) -> np.ndarray:
+        """Elements (rows[t], cols[t]) of ``igemm_tn(A, Bt)`` as int32."""
+        A, lda = _as_rows(A, "A", np.int8)
+        Bt, ldb = _as_rows(Bt, "Bt", np.int8)
+        M, K = A.shape
+        N, K2 = Bt.shape
+        if K != K2:
+            raise ValueError(f"K mismatch: A has {K}, Bt has {K2}")
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape:
+            raise ValueError("rows and cols must have the same shape")
+        out = np.empty(rows.shape, dtype=np.int32)
+        rc = self.lib.ref_igemm_tn_entries(M, N, K, A.ctypes.data, lda, Bt.ctypes.data, ldb,
+                                           rows.size, rows.ctypes.data, cols.ctypes.data,
+                                           out.ctypes.data)
+        if rc == -2:
+            raise OverflowError("an int8 dot product does not fit int32")
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.ref_num_threads())
@@ -181,6 +242,14 @@ def hgemm_tn(A, Bt, C=None):
 
 def hgemm_tn_entries(A, Bt, rows, cols, return_sums=False):
     return default().hgemm_tn_entries(A, Bt, rows, cols, return_sums)
+
+
+def igemm_tn(A, Bt, C=None):
+    return default().igemm_tn(A, Bt, C)
+
+
+def igemm_tn_entries(A, Bt, rows, cols):
+    return default().igemm_tn_entries(A, Bt, rows, cols)
 
 
 def num_threads():

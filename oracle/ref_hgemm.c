@@ -34,6 +34,15 @@
  * exponent field 0 encodes zero and subnormals m * 2^-24, field 31 encodes
  * infinity and NaN).  No half-precision hardware arithmetic is used.
  *
+ * The int8 variant (ref_igemm_tn): the INT8 mode of the same page's
+ * multi-precision scheduling (正文 paragraph 3, FP16/INT8 switching).  The page
+ * leaves its result type open; the reading taken is the exact integer sum
+ *
+ *     C[i*ldc + j] = sum_{k=0}^{K-1} A[i*lda + k] * B[j*ldb + k]
+ *
+ * over int8 operands, stored as int32 (a sum that does not fit int32 is
+ * reported, not wrapped).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see oracle/__init__.py).
  */
 #include <math.h>
@@ -164,6 +173,57 @@ int ref_hgemm_tn_entries(int64_t M, int64_t N, int64_t K,
         if (sums) sums[t] = s;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------ int8 GEMM -- */
+
+/* sum_{k=0}^{K-1} a[k] * b[k], exact in int64 (|sum| <= K * 2^14). */
+static int64_t idot(const int8_t* a, const int8_t* b, int64_t K)
+{
+    int64_t s = 0;
+    for (int64_t k = 0; k < K; ++k) s += (int64_t)a[k] * (int64_t)b[k];
+    return s;
+}
+
+static int fits_int32(int64_t s) { return s >= INT32_MIN && s <= INT32_MAX; }
+
+/* Full int8 product.  Returns 0; -1 on a bad argument; -2 when some sum does
+   not fit int32 (C is then incomplete). */
+int ref_igemm_tn(int64_t M, int64_t N, int64_t K,
+                 const int8_t* A, int64_t lda,
+                 const int8_t* B, int64_t ldb,
+                 int32_t* C, int64_t ldc)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N) return -1;
+    int bad = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(|:bad)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            const int64_t s = idot(A + i * lda, B + j * ldb, K);
+            if (fits_int32(s)) C[i * ldc + j] = (int32_t)s;
+            else bad = 1;
+        }
+    return bad ? -2 : 0;
+}
+
+/* Selected elements of the int8 product: out[t] = C[rows[t], cols[t]]. */
+int ref_igemm_tn_entries(int64_t M, int64_t N, int64_t K,
+                         const int8_t* A, int64_t lda,
+                         const int8_t* B, int64_t ldb,
+                         int64_t count, const int64_t* rows, const int64_t* cols,
+                         int32_t* out)
+{
+    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || count < 0) return -1;
+    for (int64_t t = 0; t < count; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(|:bad)
+    for (int64_t t = 0; t < count; ++t) {
+        const int64_t s = idot(A + rows[t] * lda, B + cols[t] * ldb, K);
+        if (fits_int32(s)) out[t] = (int32_t)s;
+        else bad = 1;
+    }
+    return bad ? -2 : 0;
 }
 
 /* Threads an OpenMP parallel region of this library uses. */

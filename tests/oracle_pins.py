@@ -324,9 +324,99 @@ def pin_empty(orc):
     assert np.array_equal(bits(C), np.zeros((4, 6), np.uint16))
 
 
+# ------------------------------------------------------------ int8 variant --
+
+def pin_i8_bruteforce(orc, trials: int = 80):
+    """Tiny random int8 GEMMs (extremes -128 and 127 over-represented) against
+    sums of Python integers."""
+    rng = np.random.default_rng(21)
+    for _ in range(trials):
+        M, N, K = (int(x) for x in rng.integers(1, 7, size=3))
+        A = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        Bt = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+        A[rng.random((M, K)) < 0.2] = -128
+        Bt[rng.random((N, K)) < 0.2] = 127
+        got = orc.igemm_tn(A, Bt)
+        for i in range(M):
+            for j in range(N):
+                want = sum(int(A[i, k]) * int(Bt[j, k]) for k in range(K))
+                assert int(got[i, j]) == want, f"({M},{N},{K}) ({i},{j}): {got[i, j]} vs {want}"
+
+
+def pin_i8_closed_forms(orc):
+    """All -128: every element is 16384 K; A = I: C = B; A a permutation:
+    C[i][j] = Bt[j][perm[i]]; a column of ones sums the row of the other operand."""
+    K, N = 96, 40
+    A = np.full((5, K), -128, np.int8)
+    Bt = np.full((7, K), -128, np.int8)
+    assert np.all(orc.igemm_tn(A, Bt) == 16384 * K), "all -128"
+    rng = np.random.default_rng(22)
+    Bt = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    C = orc.igemm_tn(np.eye(K, dtype=np.int8), Bt)
+    assert np.array_equal(C, Bt.T.astype(np.int32)), "identity"
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), np.int8)
+    P[np.arange(K), perm] = 1
+    assert np.array_equal(orc.igemm_tn(P, Bt), Bt.T[perm, :].astype(np.int32)), "permutation"
+    ones = np.ones((1, K), np.int8)
+    assert np.array_equal(orc.igemm_tn(ones, Bt)[0], Bt.astype(np.int64).sum(axis=1)), "row sums"
+
+
+def pin_i8_int32_limit(orc):
+    """The largest sum, 16384 K with every product (-128)(-128): K = 131071 fits
+    int32 (2147467264), K = 131072 reaches 2^31 and is reported."""
+    A = np.full((1, 131071), -128, np.int8)
+    assert int(orc.igemm_tn(A, A)[0, 0]) == 2147467264, "K = 131071"
+    A = np.full((1, 131072), -128, np.int8)
+    try:
+        orc.igemm_tn(A, A)
+    except OverflowError:
+        pass
+    else:
+        raise AssertionError("a sum of 2^31 was not reported")
+    B = np.full((1, 131072), 127, np.int8)
+    assert int(orc.igemm_tn(A, B)[0, 0]) == -128 * 127 * 131072, "negative side fits"
+
+
+def pin_i8_numpy_and_metamorphic(orc):
+    """numpy's int64 matmul gives the same integers; swapping the operands
+    transposes C; negating A (no -128 present) negates C."""
+    rng = np.random.default_rng(23)
+    M, N, K = 45, 61, 517
+    A = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    Bt = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    C = orc.igemm_tn(A, Bt)
+    assert np.array_equal(C, A.astype(np.int64) @ Bt.astype(np.int64).T), "numpy int64"
+    assert np.array_equal(orc.igemm_tn(Bt, A), C.T), "swapped roles"
+    assert np.array_equal(orc.igemm_tn(-A, Bt), -C), "negation"
+
+
+def pin_i8_strides_entries_empty(orc):
+    """Padded operands give the contiguous result and leave C's padding alone;
+    selected entries equal the full product; empty extents; K = 0 gives 0."""
+    rng = np.random.default_rng(24)
+    M, N, K = 21, 33, 70
+    Abig = rng.integers(-128, 128, size=(M, K + 9)).astype(np.int8)
+    Bbig = rng.integers(-128, 128, size=(N, K + 2)).astype(np.int8)
+    want = orc.igemm_tn(np.ascontiguousarray(Abig[:, :K]), np.ascontiguousarray(Bbig[:, :K]))
+    Cbig = np.full((M, N + 5), 777, np.int32)
+    orc.igemm_tn(Abig[:, :K], Bbig[:, :K], Cbig[:, :N])
+    assert np.array_equal(Cbig[:, :N], want), "strided"
+    assert np.all(Cbig[:, N:] == 777), "padding of C was written"
+    r = rng.integers(0, M, 200)
+    c = rng.integers(0, N, 200)
+    assert np.array_equal(orc.igemm_tn_entries(Abig[:, :K], Bbig[:, :K], r, c), want[r, c]), \
+        "entries"
+    assert orc.igemm_tn(np.zeros((0, 4), np.int8), np.ones((3, 4), np.int8)).shape == (0, 3)
+    assert np.array_equal(orc.igemm_tn(np.zeros((4, 0), np.int8), np.zeros((6, 0), np.int8)),
+                          np.zeros((4, 6), np.int32)), "K = 0"
+
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_encode_exhaustive, pin_encoding_golden,
     pin_handworked_golden, pin_bruteforce_fraction, pin_identity, pin_identity_right,
     pin_permutation, pin_small_integer, pin_numpy_crosscheck, pin_metamorphic,
     pin_strides, pin_entries, pin_empty,
+    pin_i8_bruteforce, pin_i8_closed_forms, pin_i8_int32_limit, pin_i8_numpy_and_metamorphic,
+    pin_i8_strides_entries_empty,
 ]
