@@ -25,6 +25,7 @@ __all__ = [
     "MI_HGEMM_ERR_NO_DEVICE", "MI_HGEMM_ERR_HIP", "MI_HGEMM_ERR_IO",
     "MI_HGEMM_WARN_TABLE_DEFAULTS", "MI_HGEMM_LAYOUT_TN", "MI_HGEMM_CREATE_NO_DEVICE",
     "MI_HGEMM_TUNE_EXHAUSTIVE", "MI_HGEMM_TUNE_HEURISTIC", "MI_HGEMM_TUNE_PERSIST",
+    "MI_HGEMM_TUNE_INT8", "mi_hgemm_run_i8", "mi_hgemm_plan_i8", "igemm",
     "HgemmError", "Hgemm", "hgemm", "kernel_names", "LIB_PATH",
     "mi_hgemm_create", "mi_hgemm_create_ex", "mi_hgemm_destroy", "mi_hgemm_run",
     "mi_hgemm_run_kernel", "mi_hgemm_plan", "mi_hgemm_tune", "mi_hgemm_status_string",
@@ -44,6 +45,7 @@ MI_HGEMM_CREATE_NO_DEVICE = 1
 MI_HGEMM_TUNE_EXHAUSTIVE = 1
 MI_HGEMM_TUNE_HEURISTIC = 2
 MI_HGEMM_TUNE_PERSIST = 4
+MI_HGEMM_TUNE_INT8 = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_hgemm.so")
 if not os.path.exists(LIB_PATH):
@@ -70,6 +72,10 @@ _run_kernel = _sig("mi_hgemm_run_kernel", ctypes.c_int, _p, _i32, _i32, _i32, _i
                    _i64, _p, _i64, _p, _i64, _p, _i64, ctypes.c_int, _p)
 _plan = _sig("mi_hgemm_plan", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
              ctypes.c_int, _I32P, _I32P, _I32P, _I32P)
+_run_i8 = _sig("mi_hgemm_run_i8", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+               _i64, ctypes.c_int, _p)
+_plan_i8 = _sig("mi_hgemm_plan_i8", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+                _i64, ctypes.c_int, _I32P, _I32P, _I32P, _I32P)
 _tune = _sig("mi_hgemm_tune", ctypes.c_int, _p, _i64, _i64, _i64, ctypes.c_int, _p, _u32)
 _status_string = _sig("mi_hgemm_status_string", ctypes.c_char_p, ctypes.c_int)
 _last_hip_error = _sig("mi_hgemm_last_hip_error", ctypes.c_int, _p)
@@ -107,6 +113,10 @@ def mi_hgemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN, 
     return _run(h, M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
 
 
+def mi_hgemm_run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN, stream=None):
+    return _run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
 def mi_hgemm_run_kernel(h, kernel_index, group_m, xcd_remap, split_k, M, N, K, A, lda, B, ldb,
                         C, ldc, layout=MI_HGEMM_LAYOUT_TN, stream=None):
     return _run_kernel(h, kernel_index, group_m, xcd_remap, split_k, M, N, K, A, lda, B, ldb, C,
@@ -118,6 +128,14 @@ def mi_hgemm_plan(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN)
     k, g, x, s = ctypes.c_int32(-2), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
     st = _plan(h, M, N, K, A, lda, B, ldb, C, ldc, layout, ctypes.byref(k), ctypes.byref(g),
                ctypes.byref(x), ctypes.byref(s))
+    return st, k.value, g.value, x.value, s.value
+
+
+def mi_hgemm_plan_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN):
+    """-> (status, kernel_index, group_m, xcd_remap, split_k)"""
+    k, g, x, s = ctypes.c_int32(-2), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = _plan_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout, ctypes.byref(k), ctypes.byref(g),
+                  ctypes.byref(x), ctypes.byref(s))
     return st, k.value, g.value, x.value, s.value
 
 
@@ -170,12 +188,12 @@ def _check(st, what, allow=(MI_HGEMM_OK,)):
     return st
 
 
-def _operand(x: torch.Tensor, name: str) -> int:
-    """Leading dimension (elements) of a 2-D fp16 GPU tensor with unit-stride rows."""
+def _operand(x: torch.Tensor, name: str, dtype=torch.float16) -> int:
+    """Leading dimension (elements) of a 2-D GPU tensor of ``dtype`` with unit-stride rows."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError(f"{name} must be a 2-D tensor")
-    if x.dtype != torch.float16:
-        raise TypeError(f"{name} must be float16, got {x.dtype}")
+    if x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
     if not x.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     rows, cols = x.shape
@@ -220,7 +238,10 @@ class Hgemm:
         self.close()
 
     def _args(self, A, Bt, out):
-        lda, ldb = _operand(A, "A"), _operand(Bt, "Bt")
+        """int8 A and Bt select the int8 variant (int32 result), else fp16."""
+        i8 = isinstance(A, torch.Tensor) and A.dtype == torch.int8
+        in_t, out_t = (torch.int8, torch.int32) if i8 else (torch.float16, torch.float16)
+        lda, ldb = _operand(A, "A", in_t), _operand(Bt, "Bt", in_t)
         M, K = A.shape
         N, K2 = Bt.shape
         if K != K2:
@@ -228,10 +249,10 @@ class Hgemm:
         if A.device != Bt.device:
             raise ValueError("A and Bt must be on the same device")
         if out is None:
-            out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+            out = torch.empty((M, N), dtype=out_t, device=A.device)
         elif tuple(out.shape) != (M, N):
             raise ValueError(f"out must have shape {(M, N)}")
-        ldc = _operand(out, "out")
+        ldc = _operand(out, "out", out_t)
         return M, N, K, lda, ldb, ldc, out
 
     def run(self, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
@@ -242,9 +263,26 @@ class Hgemm:
         _check(st, "mi_hgemm_run")
         return out
 
+    def run_i8(self, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+        """``A @ Bt.T`` for int8 A [M, K] and Bt [N, K], exact, as int32 [M, N]."""
+        if A.dtype != torch.int8:
+            raise TypeError(f"A must be torch.int8, got {A.dtype}")
+        M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
+        st = mi_hgemm_run_i8(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb,
+                             out.data_ptr(), ldc, MI_HGEMM_LAYOUT_TN,
+                             _stream_ptr(stream, A.device))
+        _check(st, "mi_hgemm_run_i8")
+        return out
+
     def run_kernel(self, kernel, A, Bt, out=None, group_m=1, xcd_remap=0, split_k=1,
                    stream=None):
         idx = kernel if isinstance(kernel, int) else kernel_names().index(kernel)
+        # the C ABI takes the element type from the instance: operands of the
+        # other type would be read and written with the wrong element size
+        name = mi_hgemm_kernel_name(idx)
+        if name is not None and name.startswith("i8_") != (A.dtype == torch.int8):
+            raise TypeError(f"instance {name} does not take {A.dtype} operands")
         M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
         st = mi_hgemm_run_kernel(self.handle, idx, group_m, xcd_remap, split_k, M, N, K,
                                  A.data_ptr(), lda, Bt.data_ptr(), ldb, out.data_ptr(), ldc,
@@ -253,10 +291,12 @@ class Hgemm:
         return out
 
     def plan(self, A, Bt, out=None):
-        """-> (kernel name or None, group_m, xcd_remap, split_k) that ``run`` would use."""
+        """-> (kernel name or None, group_m, xcd_remap, split_k) that ``run`` (or
+        ``run_i8``, for int8 operands) would use."""
         M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
-        st, k, g, x, s = mi_hgemm_plan(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(),
-                                       ldb, out.data_ptr(), ldc)
+        fn = mi_hgemm_plan_i8 if A.dtype == torch.int8 else mi_hgemm_plan
+        st, k, g, x, s = fn(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(),
+                            ldb, out.data_ptr(), ldc)
         _check(st, "mi_hgemm_plan")
         return (mi_hgemm_kernel_name(k) if k >= 0 else None), g, x, s
 
@@ -285,3 +325,12 @@ def hgemm(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
     if _default_handle is None:
         _default_handle = Hgemm()
     return _default_handle.run(A, Bt, out, stream)
+
+
+def igemm(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
+          stream=None) -> torch.Tensor:
+    """``A @ Bt.T`` for int8 operands, exact int32 result, on a process-wide handle."""
+    global _default_handle
+    if _default_handle is None:
+        _default_handle = Hgemm()
+    return _default_handle.run_i8(A, Bt, out, stream)

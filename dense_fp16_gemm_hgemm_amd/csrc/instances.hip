@@ -56,6 +56,24 @@ namespace mihg {
   X(256, 256)                    \
   X(256, 128)
 
+// Int8 variant (int8 operands, int32 results).  I8_D2TILE: X(BM, BN, WGM, WGN),
+// K step 128; I8_KTILE: X(BM, BN, WGM, WGN, BK, S), K step BK of 256 or 512.
+#define MIHG_I8_D2TILE_INSTANCES(X) \
+  X(256, 256, 2, 4)                 \
+  X(256, 128, 2, 2)                 \
+  X(128, 128, 2, 2)
+
+#define MIHG_I8_KTILE_INSTANCES(X) \
+  X(128, 128, 2, 4, 256, 2)        \
+  X(128, 128, 2, 2, 256, 2)        \
+  X(128, 64, 2, 2, 256, 3)         \
+  X(64, 128, 2, 2, 256, 3)         \
+  X(64, 64, 2, 2, 256, 3)          \
+  X(64, 64, 2, 2, 512, 2)          \
+  X(32, 64, 2, 2, 256, 3)          \
+  X(16, 64, 1, 4, 256, 3)          \
+  X(16, 64, 1, 4, 512, 3)
+
 // KTILE: X(BM, BN, WGM, WGN, BK, S): K step BK (128 or 256), S LDS stages
 #define MIHG_KTILE_INSTANCES(X) \
   X(64, 64, 2, 2, 128, 2)        \
@@ -98,6 +116,10 @@ namespace mihg {
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
+#define INSTANTIATE_I8_D2TILE(BM, BN, WGM, WGN) \
+  template __global__ void i8_d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_I8_KTILE(BM, BN, WGM, WGN, BK, S) \
+  template __global__ void i8_ktile_kernel<BM, BN, WGM, WGN, BK / 128, S>(GemmArgs);
 #define INSTANTIATE_SKINNY(FM, FN, W, U) \
   template __global__ void skinny_kernel<FM, FN, W, U, 2>(GemmArgs);
 template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
@@ -107,6 +129,9 @@ MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
 MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
+template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
+MIHG_I8_D2TILE_INSTANCES(INSTANTIATE_I8_D2TILE)
+MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 
 // The registry holds host launch functions, so it exists only in the host pass.
 #if !defined(__HIP_DEVICE_COMPILE__)
@@ -128,6 +153,14 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1, &launch_ktile<BM, BN, WGM, WGN, BK / 64, S>, \
    &grid_tile<BM, BN>},
+#define I8_D2TILE_DESC(BM, BN, WGM, WGN)                                                    \
+  {"i8_d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN, 16, \
+   1, 1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_i8_d2tile<BM, BN, WGM, WGN>,                   \
+   &grid_tile<BM, BN>, DTYPE_I8},
+#define I8_KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
+  {"i8_ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,        \
+   WGM * WGN, 16, 1, 1, S * (BM + BN) * BK, 1, &launch_i8_ktile<BM, BN, WGM, WGN, BK / 128, S>, \
+   &grid_tile<BM, BN>, DTYPE_I8},
 #define SKINNY_DESC(FM, FN, W, U)                                                          \
   {"skinny_" #FM "x" #FN "_w" #W "_u" #U, FAMILY_SKINNY, 16 * FM, 16 * FN, 32, W, 16, 1, U, \
    W * 16 * FM * 16 * FN * 4, 1, &launch_skinny<FM, FN, W, U, 2>, &grid_tile<16 * FM, 16 * FN>},
@@ -142,6 +175,11 @@ const KernelDesc kKernels[] = {
     MIHG_PPTILE_INSTANCES(PPTILE_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
+    // int8 variant: element-wise instance first, then the vector-load tiles
+    {"i8_generic_64x64_w2x2_m16", FAMILY_TILE, 64, 64, 128, 4, 16, 0, 1, 128 * 64 * 2, 0,
+     &launch_i8_generic<64, 64, 2, 2, 16>, &grid_tile<64, 64>, DTYPE_I8},
+    MIHG_I8_D2TILE_INSTANCES(I8_D2TILE_DESC)
+    MIHG_I8_KTILE_INSTANCES(I8_KTILE_DESC)
 };
 
 const int kNumKernels = (int)(sizeof(kKernels) / sizeof(kKernels[0]));
@@ -210,6 +248,51 @@ hipError_t launch_fill_uniform(void* X, int64_t n, uint32_t seed, float scale, h
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(fill_uniform_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      static_cast<_Float16*>(X), n, seed, scale);
+  return hipGetLastError();
+}
+
+// Int8 operands with every byte value equally likely: both the exactness check
+// and the timing data of the int8 variant (integer products are exact).
+__global__ void fill_i8_kernel(int8_t* X, int64_t n, uint32_t seed) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t h = mix32((uint32_t)t ^ mix32(seed ^ (uint32_t)(t >> 32)));
+    X[t] = (int8_t)(h >> 24);
+  }
+}
+
+hipError_t launch_fill_i8(void* X, int64_t n, uint32_t seed, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_i8_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<int8_t*>(X), n, seed);
+  return hipGetLastError();
+}
+
+__global__ void count_mismatch32_kernel(const uint32_t* X, const uint32_t* Y, int32_t M,
+                                        int32_t N, int64_t ld, int* count) {
+  const int64_t total = (int64_t)M * N;
+  int bad = 0;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = t / N, j = t - i * N;
+    bad += X[i * ld + j] != Y[i * ld + j];
+  }
+  if (bad) atomicAdd(count, bad);
+}
+
+hipError_t launch_count_mismatch32(const void* X, const void* Y, int32_t M, int32_t N, int64_t ld,
+                                   int* d_count, hipStream_t s) {
+  hipError_t e = hipMemsetAsync(d_count, 0, sizeof(int), s);
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)M * N;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(count_mismatch32_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(X), static_cast<const uint32_t*>(Y), M, N, ld,
+                     d_count);
   return hipGetLastError();
 }
 

@@ -140,6 +140,62 @@ __device__ inline void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t off, _Float
   __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// gfx950's int8 MFMA: 16 x 16 outputs over a reduction of 64, each lane
+// supplying 16 consecutive int8 values of its row (the same 16-byte fragment
+// that holds 8 halves for v_mfma_f32_16x16x32_f16), int32 accumulation.
+struct MfmaI8 {
+  static constexpr int KI = 64;
+  static constexpr int NACC = 4;
+  typedef i32x4 acc_t;
+  __device__ static inline acc_t mma(h8 a, h8 b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                 __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+  }
+};
+
+// Element types of a GEMM variant.  Every variant moves operands as 16-byte
+// lane fragments and LDS rows of 128 (or 256, 512) bytes, so copies, LDS
+// layouts and schedules are shared, and each 64 bytes of a row are one MFMA
+// K step; only the element width, the MFMA, the accumulator and the result
+// conversion differ.
+//   OpF16: binary16 operands, fp32 accumulation, binary16 result (RNE).
+//   OpI8:  int8 operands, int32 accumulation, int32 result (exact).
+struct OpF16 {
+  static constexpr int kEB = 2;  // operand bytes per element
+  static constexpr int kCB = 2;  // result bytes per element
+  typedef _Float16 in_t;
+  typedef _Float16 out_t;
+  template <int MF>
+  using Mma = Mfma<MF>;
+  // four consecutive results of one output row, at byte offset off
+  __device__ static inline void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+    h4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (_Float16)v[e];
+    buf_store8(r, off, o);
+  }
+  __device__ static inline void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    buf_store2(r, off, (_Float16)v);
+  }
+};
+
+struct OpI8 {
+  static constexpr int kEB = 1;
+  static constexpr int kCB = 4;
+  typedef int8_t in_t;
+  typedef int32_t out_t;
+  template <int MF>
+  using Mma = MfmaI8;
+  __device__ static inline void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+  }
+  __device__ static inline void store1(__amdgpu_buffer_rsrc_t r, uint32_t off, int v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Tile family: BM x BN x 64 workgroup tiles, WGM x WGN waves, 2 LDS stages,
 // operands in the 16-byte alignment class.
@@ -465,10 +521,12 @@ __device__ __forceinline__ void dtrip_schedule() {
 template <int FM, int FN, int NT, typename Acc>
 __device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs& p, int tile_id,
                                              int slice, int splitk, int tid, int* s_last) {
-  constexpr int NACC = sizeof(Acc) / sizeof(float);
-  static_assert(NACC % 4 == 0, "accumulators come in float4 groups");
-  constexpr int NV = FM * FN * (NACC / 4);  // float4 values per lane
-  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef std::remove_cv_t<std::remove_reference_t<decltype(acc[0][0][0])>> E;  // float or int
+  static_assert(sizeof(E) == 4, "32-bit accumulators");
+  constexpr int NACC = sizeof(Acc) / sizeof(E);
+  static_assert(NACC % 4 == 0, "accumulators come in groups of 4");
+  constexpr int NV = FM * FN * (NACC / 4);  // 4-element values per lane
+  typedef E f4 __attribute__((ext_vector_type(4)));
   const auto rsw = make_rsrc(reinterpret_cast<const f4*>(p.ws) + (int64_t)tile_id * splitk * (NV * NT),
                              (uint32_t)(splitk * NV * NT * 16));
 #pragma unroll
@@ -500,7 +558,7 @@ __device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs&
   for (int v0 = 0; v0 < NV; v0 += VG) {
     f4 sum[VG];
 #pragma unroll
-    for (int u = 0; u < VG; ++u) sum[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < VG; ++u) sum[u] = f4{0, 0, 0, 0};
     for (int s2 = 0; s2 < splitk; ++s2) {
       if (s2 == slice) {
 #pragma unroll
@@ -798,11 +856,12 @@ dtile_kernel(GemmArgs p) {
 // rows; its lanes need one of two global offsets (even or odd block).
 constexpr int kD2Row = 64;  // halves per LDS row
 
-template <int BM, int BN, int WGM, int WGN>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-d2tile_kernel(GemmArgs p) {
-  using MM = Mfma<16>;
-  constexpr int MF = 16, BK = 64, KSTEPS = 2;
+template <typename Op, int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
+  using MM = typename Op::template Mma<16>;
+  constexpr int EB = Op::kEB, CB = Op::kCB;
+  constexpr int MF = 16, BK = 128 / EB, KSTEPS = 2;  // BK: elements per 128-byte LDS row
+  constexpr int EPC = 16 / EB;                         // elements per 16-byte chunk
   constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
@@ -828,30 +887,30 @@ d2tile_kernel(GemmArgs p) {
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int drow = lane >> 3;
   const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
-  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
-                             (uint32_t)(min(BM, M - m0) * lda * 2));
-  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
-                             (uint32_t)(min(BN, N - n0) * ldb * 2));
-  const uint32_t a_v0 = (uint32_t)(drow * lda * 2 + dch0 * 16), a_v1 = (uint32_t)(drow * lda * 2 + dch1 * 16);
-  const uint32_t b_v0 = (uint32_t)(drow * ldb * 2 + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * 2 + dch1 * 16);
-  const bool mask_k = (K & 63) != 0;
+  const u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB,
+                             (uint32_t)(min(BM, M - m0) * lda * EB));
+  const u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB,
+                             (uint32_t)(min(BN, N - n0) * ldb * EB));
+  const uint32_t a_v0 = (uint32_t)(drow * lda * EB + dch0 * 16), a_v1 = (uint32_t)(drow * lda * EB + dch1 * 16);
+  const uint32_t b_v0 = (uint32_t)(drow * ldb * EB + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * EB + dch1 * 16);
+  const bool mask_k = (K % BK) != 0;
   const uint32_t lds0 = lds_addr(lds);
   // copy x (0..ND-1) of tile k0 into stage st
   auto dma_one = [&](int st, int k0, int x) {
-    const uint32_t kb = (uint32_t)k0 * 2;
+    const uint32_t kb = (uint32_t)k0 * EB;
     const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
     if (x < A_BLK) {
       const int blk = wave_u * A_BLK + x;
       const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (k0 + ch * 8 < K);
-      dma16(rda, kin ? ((x & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
+      const bool kin = !mask_k || (k0 + ch * EPC < K);
+      dma16(rda, kin ? ((x & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * EB) + kb,
             sbase + blk * 8 * kD2Row * 2);
     } else {
       const int xb = x - A_BLK;
       const int blk = wave_u * B_BLK + xb;
       const int ch = (xb & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (k0 + ch * 8 < K);
-      dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
+      const bool kin = !mask_k || (k0 + ch * EPC < K);
+      dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * EB) + kb,
             sbase + (BM + blk * 8) * kD2Row * 2);
     }
   };
@@ -880,7 +939,7 @@ d2tile_kernel(GemmArgs p) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0;
 
   constexpr int NM = FM * FN, NR = FM + FN;
   // One half trip: the NM MFMAs of step S_MFMA (when DO_MFMA), with the
@@ -949,8 +1008,8 @@ d2tile_kernel(GemmArgs p) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
 
-  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
-  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
   if ((N & 3) == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -958,10 +1017,7 @@ d2tile_kernel(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
-        h4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
-        buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+        Op::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, acc[fm][fn]);
       }
     }
   } else {
@@ -973,11 +1029,19 @@ d2tile_kernel(GemmArgs p) {
         const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
-                     (_Float16)acc[fm][fn][e]);
+          Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB, acc[fm][fn][e]);
       }
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tile_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN>(p);
+}
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile_kernel(GemmArgs p) {
+  d2tile_body<OpI8, BM, BN, WGM, WGN>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1196,14 +1260,16 @@ pptile_kernel(GemmArgs p) {
 // 256- and 512-byte rows.  A copy instruction fills a 1 KiB block of
 // RPB = 8/KB rows; lane l lands on row l / (8*KB) of the block, physical
 // chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
-template <int BM, int BN, int WGM, int WGN, int KB, int S>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-ktile_kernel(GemmArgs p) {
-  using MM = Mfma<16>;
-  constexpr int MF = 16, BK = 64 * KB, KSTEPS = 2 * KB;
-  constexpr int ROWH = BK;                 // halves per LDS row
-  constexpr int CPR = BK / 8;              // 16-byte chunks per LDS row
-  constexpr int RPB = 1024 / (2 * BK);     // rows per 1 KiB copy block
+template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S>
+__device__ __forceinline__ void ktile_body(const GemmArgs& p) {
+  using MM = typename Op::template Mma<16>;
+  constexpr int EB = Op::kEB, CB = Op::kCB;
+  constexpr int MF = 16, KSTEPS = 2 * KB;
+  constexpr int BK = 128 * KB / EB;        // K elements per trip (128 * KB bytes of a row)
+  constexpr int EPC = 16 / EB;             // K elements per 16-byte chunk
+  constexpr int ROWH = 64 * KB;            // halves per LDS row
+  constexpr int CPR = 8 * KB;              // 16-byte chunks per LDS row
+  constexpr int RPB = 1024 / (2 * ROWH);   // rows per 1 KiB copy block
   constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
@@ -1236,10 +1302,10 @@ ktile_kernel(GemmArgs p) {
   const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
-                             (uint32_t)(min(BM, M - m0) * lda * 2));
-  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
-                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB,
+                             (uint32_t)(min(BM, M - m0) * lda * EB));
+  const u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB,
+                             (uint32_t)(min(BN, N - n0) * ldb * EB));
   // per copy x of a trip: this lane's source offset (row and chunk) and the
   // chunk's k offset within the trip
   uint32_t c_off[ND];
@@ -1250,8 +1316,8 @@ ktile_kernel(GemmArgs p) {
     const int blk = is_a ? wave_u * A_BLK + x : wave_u * B_BLK + (x - A_BLK);
     const int row = blk * RPB + lane / CPR;
     const int c = (lane % CPR) ^ (row & 15);
-    c_off[x] = (uint32_t)(row * (is_a ? lda : ldb) * 2 + c * 16);
-    c_k[x] = c * 8;
+    c_off[x] = (uint32_t)(row * (is_a ? lda : ldb) * EB + c * 16);
+    c_k[x] = c * EPC;
   }
   const bool mask_k = ((k_end - k_begin) % BK) != 0;
   const uint32_t lds0 = lds_addr(lds);
@@ -1261,10 +1327,10 @@ ktile_kernel(GemmArgs p) {
     const bool kin = !mask_k || (k0 + c_k[x] < k_end);
     if (x < A_BLK) {
       const int blk = wave_u * A_BLK + x;
-      dma16(rda, kin ? c_off[x] : kOOB, (uint32_t)k0 * 2, sbase + (uint32_t)(blk * 1024));
+      dma16(rda, kin ? c_off[x] : kOOB, (uint32_t)k0 * EB, sbase + (uint32_t)(blk * 1024));
     } else {
       const int blk = wave_u * B_BLK + (x - A_BLK);
-      dma16(rdb, kin ? c_off[x] : kOOB, (uint32_t)k0 * 2,
+      dma16(rdb, kin ? c_off[x] : kOOB, (uint32_t)k0 * EB,
             sbase + (uint32_t)(BM * ROWH * 2 + blk * 1024));
     }
   };
@@ -1294,7 +1360,7 @@ ktile_kernel(GemmArgs p) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0;
 
   constexpr int NM = FM * FN, NR = FM + FN;
   // Part J of a trip: the NM MFMAs of step (J - 1) mod KSTEPS, with the NR
@@ -1373,8 +1439,8 @@ ktile_kernel(GemmArgs p) {
     if (!splitk_fixup<FM, FN, NT>(acc, p, tile_id, slice, splitk, tid, &s_last)) return;
   }
 
-  _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
-  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
   if ((N & 3) == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -1382,10 +1448,7 @@ ktile_kernel(GemmArgs p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
-        h4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
-        buf_store8(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, o);
+        Op::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, acc[fm][fn]);
       }
     }
   } else {
@@ -1397,11 +1460,19 @@ ktile_kernel(GemmArgs p) {
         const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          buf_store2(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
-                     (_Float16)acc[fm][fn][e]);
+          Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB, acc[fm][fn][e]);
       }
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN) ktile_kernel(GemmArgs p) {
+  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S>(p);
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_kernel(GemmArgs p) {
+  ktile_body<OpI8, BM, BN, WGM, WGN, KB, S>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1409,11 +1480,15 @@ ktile_kernel(GemmArgs p) {
 // tiling and arithmetic as the tile family, but every global access is a
 // 2-byte access with its own bounds check; it exists for operands outside the
 // 16-byte class and as the tuner's reference.
-template <int BM, int BN, int WGM, int WGN, int MF>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-generic_kernel(GemmArgs p) {
-  using MM = Mfma<MF>;
-  constexpr int BK = 64, CPR = BK / 8;
+template <typename Op, int BM, int BN, int WGM, int WGN, int MF>
+__device__ __forceinline__ void generic_body(const GemmArgs& p) {
+  using MM = typename Op::template Mma<MF>;
+  using In = typename Op::in_t;
+  using Out = typename Op::out_t;
+  constexpr int EPC = 16 / Op::kEB;      // elements per 16-byte chunk
+  constexpr int BK = 8 * EPC, CPR = 8;   // 128-byte rows of 8 chunks
+  constexpr int RH = 64;                 // halves per LDS row
+  constexpr int CPS = MM::KI / EPC;      // chunks per MFMA K step
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
@@ -1421,7 +1496,7 @@ generic_kernel(GemmArgs p) {
   constexpr int A_IT = BM * CPR / NT, B_IT = BN * CPR / NT;
   static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile chunks must split evenly");
 
-  __shared__ __attribute__((aligned(16))) _Float16 lds[(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) _Float16 lds[(BM + BN) * RH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -1429,9 +1504,9 @@ generic_kernel(GemmArgs p) {
   int tm, tn;
   tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const _Float16* __restrict__ A = static_cast<const _Float16*>(p.A);
-  const _Float16* __restrict__ B = static_cast<const _Float16*>(p.B);
-  _Float16* __restrict__ C = static_cast<_Float16*>(p.C);
+  const In* __restrict__ A = static_cast<const In*>(p.A);
+  const In* __restrict__ B = static_cast<const In*>(p.B);
+  Out* __restrict__ C = static_cast<Out*>(p.C);
   const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
   typename MM::acc_t acc[FM][FN];
@@ -1440,41 +1515,41 @@ generic_kernel(GemmArgs p) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0;
 
   for (int k0 = 0; k0 < K; k0 += BK) {
 #pragma unroll
     for (int it = 0; it < A_IT; ++it) {
       const int idx = tid + it * NT, row = idx / CPR, c = idx % CPR;
-      const int gm = m0 + row, gk = k0 + c * 8;
-      h8 v;
+      const int gm = m0 + row, gk = k0 + c * EPC;
+      In v[EPC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (gm < M && gk + e < K) ? A[gm * lda + gk + e] : (_Float16)0.0f;
-      *reinterpret_cast<h8*>(lds + row * BK + swz(row, c) * 8) = v;
+      for (int e = 0; e < EPC; ++e) v[e] = (gm < M && gk + e < K) ? A[gm * lda + gk + e] : (In)0;
+      *reinterpret_cast<h8*>(lds + row * RH + swz(row, c) * 8) = __builtin_bit_cast(h8, v);
     }
 #pragma unroll
     for (int it = 0; it < B_IT; ++it) {
       const int idx = tid + it * NT, row = idx / CPR, c = idx % CPR;
-      const int gn = n0 + row, gk = k0 + c * 8;
-      h8 v;
+      const int gn = n0 + row, gk = k0 + c * EPC;
+      In v[EPC];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (gn < N && gk + e < K) ? B[gn * ldb + gk + e] : (_Float16)0.0f;
-      *reinterpret_cast<h8*>(lds + BM * BK + row * BK + swz(row, c) * 8) = v;
+      for (int e = 0; e < EPC; ++e) v[e] = (gn < N && gk + e < K) ? B[gn * ldb + gk + e] : (In)0;
+      *reinterpret_cast<h8*>(lds + BM * RH + row * RH + swz(row, c) * 8) = __builtin_bit_cast(h8, v);
     }
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int c = ks * (MM::KI / 8) + lane / MF;
+      const int c = ks * CPS + lane / MF;
       h8 af[FM], bf[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int row = wm * WTM + fm * MF + lane % MF;
-        af[fm] = *reinterpret_cast<const h8*>(lds + row * BK + swz(row, c) * 8);
+        af[fm] = *reinterpret_cast<const h8*>(lds + row * RH + swz(row, c) * 8);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int row = wn * WTN + fn * MF + lane % MF;
-        bf[fn] = *reinterpret_cast<const h8*>(lds + BM * BK + row * BK + swz(row, c) * 8);
+        bf[fn] = *reinterpret_cast<const h8*>(lds + BM * RH + row * RH + swz(row, c) * 8);
       }
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -1495,9 +1570,19 @@ generic_kernel(GemmArgs p) {
         const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (j + e < N) C[i * ldc + j + e] = (_Float16)acc[fm][fn][4 * g + e];
+          if (j + e < N) C[i * ldc + j + e] = (Out)acc[fm][fn][4 * g + e];
       }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN) generic_kernel(GemmArgs p) {
+  generic_body<OpF16, BM, BN, WGM, WGN, MF>(p);
+}
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN) i8_generic_kernel(GemmArgs p) {
+  static_assert(MF == 16, "the int8 MFMA is 16 x 16 x 64");
+  generic_body<OpI8, BM, BN, WGM, WGN, MF>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1732,6 +1817,30 @@ template <int BM, int BN, int WGM, int WGN, int MF>
 hipError_t launch_generic(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((generic_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+hipError_t launch_i8_ktile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((i8_ktile_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_i8_d2tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((i8_d2tile_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int MF>
+hipError_t launch_i8_generic(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((i8_generic_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }

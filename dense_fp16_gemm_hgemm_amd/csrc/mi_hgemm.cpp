@@ -55,11 +55,20 @@ struct Config {
 constexpr size_t kWsBytes = size_t(64) << 20;
 constexpr int kMaxTiles = 1 << 16;
 
+// Dispatch class of a call: element type x alignment class.  Table entries and
+// the nearest-shape search never cross classes.
+enum Cls : int32_t { CLS_F16_ANY = 0, CLS_F16_A16 = 1, CLS_I8_ANY = 2, CLS_I8_A16 = 3 };
+constexpr const char* kClsName[4] = {"any", "a16", "i8any", "i8a16"};
+
+int32_t make_cls(int32_t dtype, bool aligned) { return 2 * dtype + (aligned ? 1 : 0); }
+int32_t cls_dtype(int32_t cls) { return cls / 2; }
+bool cls_aligned(int32_t cls) { return (cls & 1) != 0; }
+
 struct Key {
   int64_t M, N, K;
-  int32_t aligned;
+  int32_t cls;
   bool operator<(const Key& o) const {
-    return std::tie(M, N, K, aligned) < std::tie(o.M, o.N, o.K, o.aligned);
+    return std::tie(M, N, K, cls) < std::tie(o.M, o.N, o.K, o.cls);
   }
 };
 
@@ -86,13 +95,28 @@ int find_kernel(const char* name) {
   return -1;
 }
 
-// Shared argument checks of run, plan and run_kernel.
-mi_hgemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                           const void* B, int64_t ldb, const void* C, int64_t ldc,
+// The int8 variant's int32 sums stay exact while K * 128 * 128 < 2^31.
+constexpr int64_t kMaxKInt8 = 131071;
+
+// Element bytes of operands and result.
+int operand_bytes(int32_t dtype) { return dtype == mihg::DTYPE_I8 ? 1 : 2; }
+int result_bytes(int32_t dtype) { return dtype == mihg::DTYPE_I8 ? 4 : 2; }
+
+// Instance 0 is the fp16 element-wise instance; the int8 one is found by name.
+int generic_kernel(int32_t dtype) {
+  if (dtype == mihg::DTYPE_F16) return kGenericKernel;
+  static const int i8 = find_kernel("i8_generic_64x64_w2x2_m16");
+  return i8;
+}
+
+// Shared argument checks of run, plan and run_kernel, for element type dtype.
+mi_hgemm_status_t validate(int32_t dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                           int64_t lda, const void* B, int64_t ldb, const void* C, int64_t ldc,
                            mi_hgemm_layout_t layout) {
   if (layout != MI_HGEMM_LAYOUT_TN) return MI_HGEMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return MI_HGEMM_ERR_INVALID_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (dtype == mihg::DTYPE_I8 && K > kMaxKInt8) return MI_HGEMM_ERR_UNSUPPORTED;
   if (lda < std::max<int64_t>(K, 1) || ldb < std::max<int64_t>(K, 1) ||
       ldc < std::max<int64_t>(N, 1))
     return MI_HGEMM_ERR_INVALID_ARG;
@@ -100,12 +124,13 @@ mi_hgemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (C == nullptr) return MI_HGEMM_ERR_INVALID_ARG;
   if (K > 0 && (A == nullptr || B == nullptr)) return MI_HGEMM_ERR_INVALID_ARG;
   // C must not overlap the operands it is computed from.
+  const uintptr_t eb = (uintptr_t)operand_bytes(dtype), cb = (uintptr_t)result_bytes(dtype);
   const uintptr_t c0 = reinterpret_cast<uintptr_t>(C);
-  const uintptr_t c1 = c0 + 2u * (uintptr_t)((M - 1) * ldc + N);
+  const uintptr_t c1 = c0 + cb * (uintptr_t)((M - 1) * ldc + N);
   auto overlaps = [&](const void* X, int64_t rows, int64_t ld, int64_t cols) {
     if (rows == 0 || cols == 0) return false;
     const uintptr_t x0 = reinterpret_cast<uintptr_t>(X);
-    const uintptr_t x1 = x0 + 2u * (uintptr_t)((rows - 1) * ld + cols);
+    const uintptr_t x1 = x0 + eb * (uintptr_t)((rows - 1) * ld + cols);
     return x0 < c1 && c0 < x1;
   };
   if (K > 0 && (overlaps(A, M, lda, K) || overlaps(B, N, ldb, K))) return MI_HGEMM_ERR_INVALID_ARG;
@@ -117,9 +142,12 @@ mi_hgemm_status_t validate(int64_t M, int64_t N, int64_t K, const void* A, int64
 // then spans at most 2^30 bytes).
 constexpr int64_t kMaxVectorLd = int64_t(1) << 21;
 
-bool aligned_class(int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
-                   const void* C, int64_t ldc) {
-  return (K % 8) == 0 && (lda % 8) == 0 && (ldb % 8) == 0 && (ldc % 8) == 0 &&
+// The 16-byte class: rows of A, B and C start on 16-byte boundaries and K is
+// a whole number of 16-byte chunks (8 halves, or 16 int8 values).
+bool aligned_class(int32_t dtype, int64_t K, const void* A, int64_t lda, const void* B,
+                   int64_t ldb, const void* C, int64_t ldc) {
+  const int64_t ek = 16 / operand_bytes(dtype), ec = 16 / result_bytes(dtype);
+  return (K % ek) == 0 && (lda % ek) == 0 && (ldb % ek) == 0 && (ldc % ec) == 0 &&
          lda <= kMaxVectorLd && ldb <= kMaxVectorLd && ldc <= kMaxVectorLd &&
          is_aligned16(A) && is_aligned16(B) && is_aligned16(C);
 }
@@ -157,9 +185,11 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
 //    32x64 / 16x64 for the smallest M; small tiles are latency-bound per K
 //    step, so a deep step beats more parallel tiles;
 //  - when even those leave half the CUs idle and K is long, K is split.
-Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
+Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   Config c;
-  if (!aligned) return c;
+  const int32_t dtype = cls_dtype(cls);
+  c.kernel = generic_kernel(dtype);
+  if (!cls_aligned(cls)) return c;
   auto tiles = [&](int k) { return k >= 0 ? kKernels[k].grid((int32_t)M, (int32_t)N) : 0; };
   // as many K slices of kernel k as keep every slice >= 1024 deep and the
   // grid <= 256 workgroups (1 = no split)
@@ -177,11 +207,13 @@ Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
     c.xcd = x;
     c.splitk = s;
   };
-  const int k256 = find_kernel("d2tile_256x256_w2x4_m16");
-  const int k128 = find_kernel("ktile_128x128_w2x2_k128_s2");
-  const int k64 = find_kernel("ktile_64x64_w2x2_k128_s3");
-  const int k32 = find_kernel("ktile_32x64_w2x2_k128_s3");
-  const int k16 = find_kernel("ktile_16x64_w1x4_k128_s3");
+  // the int8 instances with the same tiles and a K step of the same bytes
+  const bool i8 = dtype == mihg::DTYPE_I8;
+  const int k256 = find_kernel(i8 ? "i8_d2tile_256x256_w2x4_m16" : "d2tile_256x256_w2x4_m16");
+  const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x2_k256_s2" : "ktile_128x128_w2x2_k128_s2");
+  const int k64 = find_kernel(i8 ? "i8_ktile_64x64_w2x2_k256_s3" : "ktile_64x64_w2x2_k128_s3");
+  const int k32 = find_kernel(i8 ? "i8_ktile_32x64_w2x2_k256_s3" : "ktile_32x64_w2x2_k128_s3");
+  const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3" : "ktile_16x64_w1x4_k128_s3");
   if (M > 64 && k256 >= 0 && tiles(k256) >= 128) {
     pick(k256, 8, 1, 1);
   } else if (M > 64 && k128 >= 0 && tiles(k128) >= 128) {
@@ -191,14 +223,14 @@ Config heuristic(int64_t M, int64_t N, int64_t K, bool aligned) {
     pick(k64, s > 1 ? 1 : 8, s > 1 ? 0 : 1, s);
   } else if (M > 16 && k32 >= 0) {
     pick(k32, 1, 0, split_for(k32));
-  } else if (k16 >= 0 && (tiles(k16) >= 128 || K >= 8192)) {
+  } else if (k16 >= 0 && (i8 || tiles(k16) >= 128 || K >= 8192)) {
     pick(k16, 1, 0, split_for(k16));
   } else {
     // 16 rows or fewer over a short K: B streamed straight into registers
     const int ks = find_kernel("skinny_1x1_w4_u4");
     pick(ks >= 0 ? ks : kGenericKernel, 1, 0, 1);
   }
-  if (c.kernel < 0) c.kernel = kGenericKernel;
+  if (c.kernel < 0) c.kernel = generic_kernel(dtype);
   return c;
 }
 
@@ -211,15 +243,15 @@ Config checked(Config c, int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
-Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
-  const Key key{M, N, K, aligned ? 1 : 0};
+Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls) {
+  const Key key{M, N, K, cls};
   auto it = h->table.find(key);
   if (it != h->table.end()) return checked(it->second, M, N, K);
   // nearest tuned shape in log2(M, N, K), within a factor of two overall
   double best = 1.0 + 1e-9;
   const Config* pick = nullptr;
   for (const auto& kv : h->table) {
-    if (kv.first.aligned != key.aligned) continue;
+    if (kv.first.cls != key.cls) continue;
     const double d = std::fabs(std::log2((double)M / kv.first.M)) +
                      std::fabs(std::log2((double)N / kv.first.N)) +
                      std::fabs(std::log2((double)K / kv.first.K));
@@ -229,11 +261,13 @@ Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, bool aligned) {
     }
   }
   if (pick) return checked(*pick, M, N, K);
-  return heuristic(M, N, K, aligned);
+  return heuristic(M, N, K, cls);
 }
 
 // Table file: one entry per line,
-//   <arch> <M> <N> <K> <layout> <a16|any> <kernel name> <group_m> <xcd_remap> <microseconds> [<split_k>]
+//   <arch> <M> <N> <K> <layout> <class> <kernel name> <group_m> <xcd_remap> <microseconds> [<split_k>]
+// with class a16 / any (fp16 in / outside the 16-byte class) or i8a16 / i8any
+// (the int8 variant).
 // '#' starts a comment.  Lines for another arch or layout are skipped; lines
 // that do not parse, or name an unknown kernel, mark the table as damaged.
 bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
@@ -262,9 +296,11 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
     }
     if (std::strcmp(arch, kArch) != 0 || std::strcmp(layout, "TN") != 0) continue;
     const int k = find_kernel(kname);
-    const bool al = std::strcmp(align, "a16") == 0;
-    if (k < 0 || (!al && std::strcmp(align, "any") != 0) || (!al && kKernels[k].aligned) ||
-        (sk > 1 && !kKernels[k].splitk_ok)) {
+    int cls = -1;
+    for (int i = 0; i < 4; ++i)
+      if (std::strcmp(align, kClsName[i]) == 0) cls = i;
+    if (k < 0 || cls < 0 || kKernels[k].dtype != cls_dtype(cls) ||
+        (!cls_aligned(cls) && kKernels[k].aligned) || (sk > 1 && !kKernels[k].splitk_ok)) {
       clean = false;
       continue;
     }
@@ -274,7 +310,7 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
     c.xcd = xcd;
     c.splitk = sk;
     c.us = us;
-    h->table[Key{M, N, K, al ? 1 : 0}] = c;
+    h->table[Key{M, N, K, cls}] = c;
   }
   std::fclose(f);
   return clean;
@@ -282,7 +318,7 @@ bool load_table(mi_hgemm_ctx* h, const std::string& path, bool* file_missing) {
 
 bool write_entry(FILE* f, const Key& k, const Config& c) {
   return std::fprintf(f, "%s %lld %lld %lld TN %s %s %d %d %.3f %d\n", kArch, (long long)k.M,
-                      (long long)k.N, (long long)k.K, k.aligned ? "a16" : "any",
+                      (long long)k.N, (long long)k.K, kClsName[k.cls],
                       kKernels[c.kernel].name, c.group_m, c.xcd, c.us, c.splitk) > 0;
 }
 
@@ -356,19 +392,57 @@ mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N,
   return MI_HGEMM_OK;
 }
 
-mi_hgemm_status_t run_config(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N, int64_t K,
-                             const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                             int64_t ldc, void* stream) {
+mi_hgemm_status_t run_config(mi_hgemm_ctx* h, int32_t dtype, const Config& c, int64_t M,
+                             int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                             int64_t ldb, void* C, int64_t ldc, void* stream) {
   if (M == 0 || N == 0) return MI_HGEMM_OK;
   if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
   DeviceGuard g(h->device);
   if (g.err != hipSuccess) return hip_fail(h, g.err);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) {
-    const hipError_t e = mihg::launch_zero_fill(C, ldc, (int32_t)M, (int32_t)N, s);
+    // +0 in binary16 and 0 in int32 are all-zero bits: an int32 row is cleared
+    // as twice as many halves
+    const int64_t w = result_bytes(dtype) / 2;
+    if (N * w > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+    const hipError_t e = mihg::launch_zero_fill(C, ldc * w, (int32_t)M, (int32_t)(N * w), s);
     return e == hipSuccess ? MI_HGEMM_OK : hip_fail(h, e);
   }
   return launch(h, c, M, N, K, A, lda, B, ldb, C, ldc, s);
+}
+
+mi_hgemm_status_t plan_impl(mi_hgemm_ctx* h, int32_t dtype, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t lda, const void* B, int64_t ldb,
+                            const void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                            int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
+                            int32_t* split_k) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  Config c;
+  c.kernel = -1;
+  if (M > 0 && N > 0 && K > 0)
+    c = select(h, M, N, K, make_cls(dtype, aligned_class(dtype, K, A, lda, B, ldb, C, ldc)));
+  if (kernel_index) *kernel_index = c.kernel;
+  if (group_m) *group_m = c.group_m;
+  if (xcd_remap) *xcd_remap = c.xcd;
+  if (split_k) *split_k = c.kernel >= 0 ? c.splitk : 1;
+  return MI_HGEMM_OK;
+}
+
+mi_hgemm_status_t run_impl(mi_hgemm_ctx* h, int32_t dtype, int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                           int64_t ldc, mi_hgemm_layout_t layout, void* stream) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  if (M == 0 || N == 0) return MI_HGEMM_OK;
+  Config c;
+  c.kernel = generic_kernel(dtype);
+  if (K > 0)
+    c = select(h, M, N, K, make_cls(dtype, aligned_class(dtype, K, A, lda, B, ldb, C, ldc)));
+  if (c.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
+  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 }  // namespace
@@ -474,29 +548,29 @@ mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64
                                 const void* C, int64_t ldc, mi_hgemm_layout_t layout,
                                 int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
                                 int32_t* split_k) {
-  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
-  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
-  if (st != MI_HGEMM_OK) return st;
-  Config c;
-  c.kernel = -1;
-  if (M > 0 && N > 0 && K > 0) c = select(h, M, N, K, aligned_class(K, A, lda, B, ldb, C, ldc));
-  if (kernel_index) *kernel_index = c.kernel;
-  if (group_m) *group_m = c.group_m;
-  if (xcd_remap) *xcd_remap = c.xcd;
-  if (split_k) *split_k = c.kernel >= 0 ? c.splitk : 1;
-  return MI_HGEMM_OK;
+  return plan_impl(h, mihg::DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, layout, kernel_index,
+                   group_m, xcd_remap, split_k);
+}
+
+mi_hgemm_status_t mi_hgemm_plan_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                                   const void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                   int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
+                                   int32_t* split_k) {
+  return plan_impl(h, mihg::DTYPE_I8, M, N, K, A, lda, B, ldb, C, ldc, layout, kernel_index,
+                   group_m, xcd_remap, split_k);
 }
 
 mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
                                const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                                int64_t ldc, mi_hgemm_layout_t layout, void* stream) {
-  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
-  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
-  if (st != MI_HGEMM_OK) return st;
-  if (M == 0 || N == 0) return MI_HGEMM_OK;
-  Config c;
-  if (K > 0) c = select(h, M, N, K, aligned_class(K, A, lda, B, ldb, C, ldc));
-  return run_config(h, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return run_impl(h, mihg::DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                                  int64_t ldc, mi_hgemm_layout_t layout, void* stream) {
+  return run_impl(h, mihg::DTYPE_I8, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
 }
 
 mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index, int32_t group_m,
@@ -510,16 +584,17 @@ mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
   if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1) || split_k < 1 || split_k > 64)
     return MI_HGEMM_ERR_INVALID_ARG;
   if (split_k > 1 && !kKernels[kernel_index].splitk_ok) return MI_HGEMM_ERR_UNSUPPORTED;
-  const mi_hgemm_status_t st = validate(M, N, K, A, lda, B, ldb, C, ldc, layout);
+  const int32_t dtype = kKernels[kernel_index].dtype;
+  const mi_hgemm_status_t st = validate(dtype, M, N, K, A, lda, B, ldb, C, ldc, layout);
   if (st != MI_HGEMM_OK) return st;
-  if (kKernels[kernel_index].aligned && !aligned_class(K, A, lda, B, ldb, C, ldc))
+  if (kKernels[kernel_index].aligned && !aligned_class(dtype, K, A, lda, B, ldb, C, ldc))
     return MI_HGEMM_ERR_UNSUPPORTED;
   Config c;
   c.kernel = kernel_index;
   c.group_m = group_m;
   c.xcd = xcd_remap;
   c.splitk = split_k;
-  return run_config(h, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 int mi_hgemm_table_size(mi_hgemm_handle_t h) {
@@ -568,15 +643,16 @@ struct TimingStream {
 // Capture `reps` launches of one candidate on stream `ts` into a graph and
 // time 5 replays; appends microseconds per launch to `trials`.
 // The timing operands: nsets copies of (A, B) back to back, set i at
-// base + i * (M + N) * K halves (A first).
+// base + i * (M + N) * K elements of eb bytes (A first).
 struct TimingSets {
-  _Float16* base = nullptr;
+  char* base = nullptr;
   int nsets = 1;
+  int eb = 2;
   const void* A(int64_t M, int64_t N, int64_t K, int i) const {
-    return base + (int64_t)i * (M + N) * K;
+    return base + ((int64_t)i * (M + N) * K) * eb;
   }
   const void* B(int64_t M, int64_t N, int64_t K, int i) const {
-    return base + (int64_t)i * (M + N) * K + M * K;
+    return base + ((int64_t)i * (M + N) * K + M * K) * eb;
   }
 };
 
@@ -623,43 +699,57 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   if (layout != MI_HGEMM_LAYOUT_TN) return MI_HGEMM_ERR_UNSUPPORTED;
   if (M < 1 || N < 1 || K < 1) return MI_HGEMM_ERR_INVALID_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
+  const int32_t dtype = (flags & MI_HGEMM_TUNE_INT8) ? mihg::DTYPE_I8 : mihg::DTYPE_F16;
+  const int eb = operand_bytes(dtype), cb = result_bytes(dtype);
   // Only the 16-byte class has a choice to make; K and N must allow it.
-  if (K % 8 != 0 || K > kMaxVectorLd || N > kMaxVectorLd) return MI_HGEMM_ERR_UNSUPPORTED;
-  // Integer scratch operands stay exact in fp32 only while 16*K < 2^24.
-  if (K >= (1 << 20)) return MI_HGEMM_ERR_UNSUPPORTED;
+  if (K % (16 / eb) != 0 || K > kMaxVectorLd || N > kMaxVectorLd) return MI_HGEMM_ERR_UNSUPPORTED;
+  // fp16: integer scratch operands stay exact in fp32 only while 16*K < 2^24;
+  // int8: the int32 sums stay exact.
+  if (dtype == mihg::DTYPE_F16 ? K >= (1 << 20) : K > kMaxKInt8) return MI_HGEMM_ERR_UNSUPPORTED;
   if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
   DeviceGuard g(h->device);
   if (g.err != hipSuccess) return hip_fail(h, g.err);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t ldc = (N + 7) / 8 * 8;
+  const int64_t ldc = (N + 16 / cb - 1) / (16 / cb) * (16 / cb);
 
-  // a, b: small integers, for the bit-exact check.  Timing sets: random
-  // mantissas scaled by 1/sqrt(K) (the clock depends on the data), in as many
-  // copies as make 2.2x the 256 MiB MALL (at most 64 copies and 4 GiB), so
-  // that the timed launches read their operands from HBM.
+  // a, b: small integers (fp16) or uniform int8, for the bit-exact check.
+  // Timing sets: random mantissas scaled by 1/sqrt(K) (the clock depends on the
+  // data), or uniform int8, in as many copies as make 2.2x the 256 MiB MALL (at
+  // most 64 copies and 4 GiB), so that the timed launches read their operands
+  // from HBM.
   Scratch a, b, tsets, c, cref, cnt;
   hipError_t e;
-  const double set_bytes = (double)(M + N) * K * 2;
+  const double set_bytes = (double)(M + N) * K * eb;
   TimingSets sets;
+  sets.eb = eb;
   sets.nsets = (int)std::max(1.0, std::min({64.0, std::ceil(2.2 * 256.0 * 1048576.0 / set_bytes),
                                             std::floor(4.0 * 1073741824.0 / set_bytes)}));
-  if ((e = hipMalloc(&a.p, (size_t)M * K * 2)) != hipSuccess) return hip_fail(h, e);
-  if ((e = hipMalloc(&b.p, (size_t)N * K * 2)) != hipSuccess) return hip_fail(h, e);
-  if ((e = hipMalloc(&tsets.p, (size_t)sets.nsets * (M + N) * K * 2)) != hipSuccess)
+  if ((e = hipMalloc(&a.p, (size_t)M * K * eb)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&b.p, (size_t)N * K * eb)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&tsets.p, (size_t)sets.nsets * (M + N) * K * eb)) != hipSuccess)
     return hip_fail(h, e);
-  sets.base = static_cast<_Float16*>(tsets.p);
-  if ((e = hipMalloc(&c.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
-  if ((e = hipMalloc(&cref.p, (size_t)M * ldc * 2)) != hipSuccess) return hip_fail(h, e);
+  sets.base = static_cast<char*>(tsets.p);
+  if ((e = hipMalloc(&c.p, (size_t)M * ldc * cb)) != hipSuccess) return hip_fail(h, e);
+  if ((e = hipMalloc(&cref.p, (size_t)M * ldc * cb)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cnt.p, sizeof(int))) != hipSuccess) return hip_fail(h, e);
-  if ((e = mihg::launch_fill_small_int(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
-  if ((e = mihg::launch_fill_small_int(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
-  const float tscale = 1.0f / std::sqrt((float)K);
-  if ((e = mihg::launch_fill_uniform(tsets.p, (int64_t)sets.nsets * (M + N) * K, 0x9abcu, tscale,
-                                     s)) != hipSuccess)
-    return hip_fail(h, e);
+  const int64_t nset_elems = (int64_t)sets.nsets * (M + N) * K;
+  if (dtype == mihg::DTYPE_F16) {
+    if ((e = mihg::launch_fill_small_int(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
+    if ((e = mihg::launch_fill_small_int(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
+    const float tscale = 1.0f / std::sqrt((float)K);
+    if ((e = mihg::launch_fill_uniform(tsets.p, nset_elems, 0x9abcu, tscale, s)) != hipSuccess)
+      return hip_fail(h, e);
+  } else {
+    if ((e = mihg::launch_fill_i8(a.p, M * K, 0x1234u, s)) != hipSuccess) return hip_fail(h, e);
+    if ((e = mihg::launch_fill_i8(b.p, N * K, 0x5678u, s)) != hipSuccess) return hip_fail(h, e);
+    if ((e = mihg::launch_fill_i8(tsets.p, nset_elems, 0x9abcu, s)) != hipSuccess)
+      return hip_fail(h, e);
+  }
 
   // Reference result: the element-wise instance.
   Config ref;
+  ref.kernel = generic_kernel(dtype);
+  if (ref.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
   mi_hgemm_status_t st = launch(h, ref, M, N, K, a.p, K, b.p, K, cref.p, ldc, s);
   if (st != MI_HGEMM_OK) return st;
 
@@ -677,7 +767,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     return hip_fail(h, e);
   }
   const bool heuristic_only = (flags & MI_HGEMM_TUNE_HEURISTIC) != 0;
-  const Config start = heuristic(M, N, K, true);
+  const Config start = heuristic(M, N, K, make_cls(dtype, true));
   std::vector<Config> cands;
   // split K when the output tiles alone leave CUs idle
   auto add_splits = [&](int k) {
@@ -695,7 +785,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   };
   for (int k = 0; k < kNumKernels; ++k) {
     const KernelDesc& kd = kKernels[k];
-    if (!kd.aligned) continue;
+    if (!kd.aligned || kd.dtype != dtype) continue;
     if (kd.grid((int32_t)M, (int32_t)N) > INT32_MAX) continue;
     if (kd.family == mihg::FAMILY_TILE) {
       static const int rasters[][2] = {{1, 0}, {4, 0}, {8, 0}, {16, 0}, {1, 1}, {4, 1}, {8, 1}, {16, 1}};
@@ -733,8 +823,12 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
       result = st;
       break;
     }
-    if ((e = mihg::launch_count_mismatch(c.p, cref.p, (int32_t)M, (int32_t)N, ldc,
-                                         static_cast<int*>(cnt.p), s)) != hipSuccess) {
+    e = dtype == mihg::DTYPE_F16
+            ? mihg::launch_count_mismatch(c.p, cref.p, (int32_t)M, (int32_t)N, ldc,
+                                          static_cast<int*>(cnt.p), s)
+            : mihg::launch_count_mismatch32(c.p, cref.p, (int32_t)M, (int32_t)N, ldc,
+                                            static_cast<int*>(cnt.p), s);
+    if (e != hipSuccess) {
       result = hip_fail(h, e);
       break;
     }
@@ -778,7 +872,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   if (result != MI_HGEMM_OK) return result;
   if (best.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
 
-  const Key key{M, N, K, 1};
+  const Key key{M, N, K, make_cls(dtype, true)};
   {
     std::lock_guard<std::mutex> lk(h->mu);
     h->table[key] = best;

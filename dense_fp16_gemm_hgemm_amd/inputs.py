@@ -17,6 +17,10 @@ Workload families (the shapes and value distributions the benchmark names):
                (4096, 11008), (14336, 4096)}; activations A = randn, weights
                B = randn * 0.02; problem index t uses seed 5 + t
   * ``square`` (8192, 8192, 8192), randn / sqrt(8192), seed 6
+
+The int8 variant's operands (``kind="i8"``) are int8 uniform over [-128, 127],
+drawn with ``rng.integers`` (A first, then B); ``i8_square`` is the 8192^3
+problem with seed 7 and ``i8_llm`` the LLM shapes with seeds 40 + t.
 """
 from __future__ import annotations
 
@@ -36,7 +40,7 @@ class Problem:
     M: int
     N: int
     K: int
-    kind: str = "randn"      # "randn" | "int" | "identity" | "perm"
+    kind: str = "randn"      # "randn" | "int" | "identity" | "perm" | "i8"
     a_scale: float = 1.0
     b_scale: float = 1.0
     seed: int = 0
@@ -47,7 +51,10 @@ class Problem:
 
     @property
     def min_bytes(self) -> int:
-        """A and B read once, C written once (beta = 0), binary16."""
+        """A and B read once, C written once (beta = 0): binary16, or int8
+        operands and an int32 result."""
+        if self.kind == "i8":
+            return self.M * self.K + self.N * self.K + 4 * self.M * self.N
         return 2 * (self.M * self.K + self.N * self.K + self.M * self.N)
 
 
@@ -63,10 +70,18 @@ def int_f16(rng: np.random.Generator, shape, lo: int = -4, hi: int = 4) -> np.nd
     return rng.integers(lo, hi + 1, size=shape).astype(np.float16)
 
 
+def int8_uniform(rng: np.random.Generator, shape) -> np.ndarray:
+    """int8 values, every one of the 256 equally likely."""
+    return rng.integers(-128, 128, size=shape).astype(np.int8)
+
+
 def make(p: Problem) -> tuple[np.ndarray, np.ndarray]:
-    """Materialise (A[M,K], Bt[N,K]) as contiguous float16 arrays."""
+    """Materialise (A[M,K], Bt[N,K]) as contiguous float16 (int8 for kind "i8") arrays."""
     rng = np.random.default_rng(p.seed)
-    if p.kind == "randn":
+    if p.kind == "i8":
+        A = int8_uniform(rng, (p.M, p.K))
+        Bt = int8_uniform(rng, (p.N, p.K))
+    elif p.kind == "randn":
         A = randn_f16(rng, (p.M, p.K), p.a_scale)
         Bt = randn_f16(rng, (p.N, p.K), p.b_scale)
     elif p.kind == "int":
@@ -123,6 +138,20 @@ def sweep(count: int = 1000) -> list[Problem]:
         m, n, k = (1 << int(x) for x in e[i])
         s = 1.0 / math.sqrt(k)
         out.append(Problem(f"sweep{i}_{m}x{n}x{k}", m, n, k, "randn", s, s, 1000 + i))
+    return out
+
+
+def i8_square(n: int = 8192) -> Problem:
+    return Problem(f"i8_square_{n}", n, n, n, "i8", seed=7)
+
+
+def i8_llm() -> list[Problem]:
+    out = []
+    t = 0
+    for m in LLM_M:
+        for n, k in LLM_NK:
+            out.append(Problem(f"i8_llm_{m}x{n}x{k}", m, n, k, "i8", seed=40 + t))
+            t += 1
     return out
 
 

@@ -72,6 +72,7 @@ typedef enum {
 #define MI_HGEMM_TUNE_EXHAUSTIVE 1u   /* every compiled instance x raster setting (default) */
 #define MI_HGEMM_TUNE_HEURISTIC 2u    /* a pruned candidate list around the built-in choice */
 #define MI_HGEMM_TUNE_PERSIST 4u      /* append the winner to the handle's table file */
+#define MI_HGEMM_TUNE_INT8 8u         /* tune the int8 variant (mi_hgemm_run_i8) for the shape */
 
 /*
  * Create a handle on the current HIP device.
@@ -113,6 +114,33 @@ mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_
                                void* C, int64_t ldc, mi_hgemm_layout_t layout, void* stream);
 
 /*
+ * The int8 variant: for 0 <= i < M and 0 <= j < N,
+ *
+ *     C[i*ldc + j] = sum_{k=0}^{K-1} A[i*lda + k] * B[j*ldb + k]
+ *
+ * with A (M x K, row-major) and B (K x N, column-major) of int8_t and C
+ * (M x N, row-major) of int32_t; the sum is exact.  This is the INT8 mode of
+ * the pages' multi-precision scheduling ("RL驱动CUDA L2 GEMM内核自动调优：
+ * A100/H100 tile size与融合优化" (blog.hotdry.top, 2025-12-05), 正文
+ * paragraph 3: FP16/INT8 switching, with the K tile doubled under INT8 to
+ * use the higher peak).  The pages leave the result type open; int32 is
+ * taken, so that the result is exact (v_mfma_i32_16x16x64_i8 accumulates in
+ * int32).  The K step of every int8 instance is twice its fp16 sibling's in
+ * elements (the same bytes per LDS row).
+ *   Arguments, sizes, leading dimensions (in elements), the empty-output and
+ *   overlap rules and the return codes are those of mi_hgemm_run; K == 0
+ *   writes 0.  K > 131071 returns UNSUPPORTED (beyond it the int32 sum of
+ *   (-128)*(-128) products can overflow).
+ * Alignment: the 16-byte class is A, B, C 16-byte aligned, K, lda, ldb
+ * multiples of 16, ldc a multiple of 4, every ld at most 2^21; anything else
+ * runs the element-wise int8 instance.  Misalignment is never an error.
+ * Split-K partial tiles are int32, summed in slice order (exact in any order).
+ */
+mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                                  void* C, int64_t ldc, mi_hgemm_layout_t layout, void* stream);
+
+/*
  * Search the compiled instances, raster settings and K splits for the shape
  * (M, N, K) in the 16-byte alignment class.  Each candidate is first run on
  * library-owned small-integer operands, on which every correct candidate gives
@@ -124,6 +152,9 @@ mi_hgemm_status_t mi_hgemm_run(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_
  * (at most 64 copies and 4 GiB), so each reads its operands from HBM as in
  * real use.  The fastest correct one becomes the handle's entry for the shape.
  * With MI_HGEMM_TUNE_PERSIST the entry is appended to the handle's table file.
+ * With MI_HGEMM_TUNE_INT8 the int8 instances are searched instead (K a
+ * multiple of 16 and at most 131071); their check and timing operands are
+ * uniform random int8 and the reference is the element-wise int8 instance.
  * Synchronises `stream`.  Allocates scratch (the operand sets and two
  * outputs, freed before returning).
  * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
@@ -155,6 +186,13 @@ mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64
                                 int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
                                 int32_t* split_k);
 
+/* mi_hgemm_plan for mi_hgemm_run_i8's arguments. */
+mi_hgemm_status_t mi_hgemm_plan_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                                   const void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                   int32_t* kernel_index, int32_t* group_m, int32_t* xcd_remap,
+                                   int32_t* split_k);
+
 /*
  * mi_hgemm_run with a forced instance, raster setting and K split (tests,
  * benchmarks, external tuners).  Validation as mi_hgemm_run, plus
@@ -162,7 +200,9 @@ mi_hgemm_status_t mi_hgemm_plan(mi_hgemm_handle_t h, int64_t M, int64_t N, int64
  * not in it, kernel_index is out of range, split_k > 1 is asked of an
  * instance without split-K, or the partial tiles exceed the workspace.
  * group_m >= 1; xcd_remap 0 or 1; 1 <= split_k <= 64 (the effective split may
- * be smaller: slices are whole multiples of 64 in K).
+ * be smaller: slices are whole multiples of 64 in K).  Instances whose name
+ * starts with "i8_" are int8 instances: their operands, result and checks are
+ * those of mi_hgemm_run_i8.
  */
 mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
                                       int32_t group_m, int32_t xcd_remap, int32_t split_k,

@@ -264,3 +264,118 @@ def test_create_rejects_null_out():
     lib.mi_hgemm_create.restype = ctypes.c_int
     lib.mi_hgemm_create.argtypes = [ctypes.c_void_p, ctypes.c_char_p]
     assert lib.mi_hgemm_create(None, None) == mh.MI_HGEMM_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ int8 variant --
+
+def plan_i8(h, M, N, K, lda=None, ldb=None, ldc=None, A=A0, B=B0, C=C0, layout=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return mh.mi_hgemm_plan_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout)
+
+
+def test_int8_registry_and_validation(inspect_handle):
+    h = inspect_handle
+    names = mh.kernel_names()
+    i8 = [n for n in names if n.startswith("i8_")]
+    assert "i8_generic_64x64_w2x2_m16" in i8 and len(i8) >= 8
+    ok, bad, uns = mh.MI_HGEMM_OK, mh.MI_HGEMM_ERR_INVALID_ARG, mh.MI_HGEMM_ERR_UNSUPPORTED
+    assert plan_i8(h, 64, 64, 64)[0] == ok
+    assert plan_i8(h, 64, 64, 64, lda=63)[0] == bad
+    assert plan_i8(h, 64, 64, 64, layout=1)[0] == uns
+    # the int32 sum is exact up to K = 131071
+    assert plan_i8(h, 4, 4, 131071)[0] == ok
+    assert plan_i8(h, 4, 4, 131072)[0] == uns
+    assert plan(h, 4, 4, 131072)[0] == ok                  # the fp16 path has no such limit
+    # overlap is measured in the variant's element sizes: int8 operands, int32 C
+    assert plan_i8(h, 64, 64, 64, C=B0 + 64 * 64 - 1)[0] == bad
+    assert plan_i8(h, 64, 64, 64, C=B0 + 64 * 64)[0] == ok
+    assert plan_i8(h, 64, 64, 64, A=C0 + 4 * 64 * 64 - 4, C=C0)[0] == bad
+    assert plan_i8(h, 64, 64, 64, A=C0 + 4 * 64 * 64, C=C0)[0] == ok
+    # K == 0 launches only the fill
+    assert plan_i8(h, 64, 64, 0, lda=1, ldb=1, A=0, B=0)[:2] == (ok, -1)
+
+
+def test_int8_alignment_class_and_heuristic(inspect_handle):
+    h = inspect_handle
+    names = mh.kernel_names()
+    generic = names.index("i8_generic_64x64_w2x2_m16")
+
+    def choice(M, N, K, **kw):
+        r = plan_i8(h, M, N, K, **kw)
+        assert r[0] == mh.MI_HGEMM_OK
+        return names[r[1]], r[4]
+
+    for M, N, K in ((8192, 8192, 8192), (1024, 4096, 4096), (64, 4096, 11008), (16, 4096, 4096)):
+        n, _ = choice(M, N, K)
+        assert n.startswith("i8_") and n != names[generic], (M, N, K, n)
+    assert choice(8192, 8192, 8192)[0] == "i8_d2tile_256x256_w2x4_m16"
+    assert choice(1024, 4096, 4096)[0] == "i8_ktile_128x128_w2x2_k256_s2"
+    assert choice(16, 4096, 4096)[0] == "i8_ktile_16x64_w1x4_k256_s3"
+    # the 16-byte class in int8 elements: K, lda, ldb multiples of 16, ldc of 4
+    assert plan_i8(h, 256, 256, 264)[1] == generic              # K = 8 mod 16
+    assert plan_i8(h, 256, 256, 256, lda=264)[1] == generic
+    assert plan_i8(h, 256, 256, 256, ldb=272)[1] != generic
+    assert plan_i8(h, 256, 256, 256, ldc=260)[1] != generic     # 4 int32 = 16 bytes
+    assert plan_i8(h, 256, 256, 256, ldc=258)[1] == generic
+    assert plan_i8(h, 256, 256, 256, A=A0 + 8)[1] == generic
+
+
+def test_int8_instances_refuse_fp16_class_and_vice_versa(inspect_handle):
+    """run_kernel validates with the instance's own element type: an int8
+    instance checks int8 alignment rules, and fp16 rules stay with fp16."""
+    h = inspect_handle
+    names = mh.kernel_names()
+    k = names.index("i8_ktile_64x64_w2x2_k256_s3")
+    # K = 40 is in the fp16 16-byte class but not the int8 one
+    assert mh.mi_hgemm_run_kernel(h, k, 1, 0, 1, 64, 64, 40, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_UNSUPPORTED
+    assert mh.mi_hgemm_run_kernel(h, k, 1, 0, 1, 64, 64, 48, A0, 64, B0, 64, C0, 64) == \
+        mh.MI_HGEMM_ERR_NO_DEVICE
+    assert mh.mi_hgemm_run_kernel(h, k, 1, 0, 1, 64, 64, 131072, A0, 131072, B0, 131072, C0,
+                                  64) == mh.MI_HGEMM_ERR_UNSUPPORTED
+
+
+def test_int8_table_classes(tmp_path, monkeypatch):
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    names = mh.kernel_names()
+    p = tmp_path / "i8.tsv"
+    write_table(p, ["gfx950 1024 4096 4096 TN i8a16 i8_ktile_64x128_w2x2_k256_s3 4 1 30.0 2",
+                    "gfx950 1024 4096 4096 TN a16 ktile_64x64_w2x2_k128_s3 8 0 40.0 1",
+                    "gfx950 77 77 77 TN i8any i8_generic_64x64_w2x2_m16 1 0 2.0"])
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK and mh.mi_hgemm_table_size(h) == 3
+    try:
+        r = plan_i8(h, 1024, 4096, 4096)
+        assert names[r[1]] == "i8_ktile_64x128_w2x2_k256_s3" and r[2:] == (4, 1, 2)
+        r = plan(h, 1024, 4096, 4096)                 # same shape, fp16 entry
+        assert names[r[1]] == "ktile_64x64_w2x2_k128_s3" and r[2:] == (8, 0, 1)
+        out = tmp_path / "saved.tsv"
+        assert mh.mi_hgemm_table_save(h, str(out)) == mh.MI_HGEMM_OK
+        text = out.read_text()
+        assert " i8a16 i8_ktile_64x128_w2x2_k256_s3 " in text and " i8any " in text
+    finally:
+        mh.mi_hgemm_destroy(h)
+    # an entry whose kernel does not match its class marks the table as damaged
+    write_table(p, ["gfx950 64 64 64 TN i8a16 ktile_64x64_w2x2_k128_s3 1 0 1.0",
+                    "gfx950 64 64 64 TN a16 i8_ktile_64x64_w2x2_k256_s3 1 0 1.0",
+                    "gfx950 64 64 64 TN i8any i8_ktile_64x64_w2x2_k256_s3 1 0 1.0"])
+    st, h = mh.mi_hgemm_create_ex(str(p), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_WARN_TABLE_DEFAULTS and mh.mi_hgemm_table_size(h) == 0
+    mh.mi_hgemm_destroy(h)
+
+
+def test_run_kernel_rejects_operands_of_the_other_type():
+    """The binding refuses to pair an instance with tensors of the other element
+    type, before anything reaches the C ABI (it needs no GPU)."""
+    h = mh.Hgemm(inspect_only=True)
+    try:
+        a = torch.zeros((4, 16), dtype=torch.float16)
+        with pytest.raises(TypeError):
+            h.run_kernel("i8_ktile_64x64_w2x2_k256_s3", a, a)
+        b = torch.zeros((4, 16), dtype=torch.int8)
+        with pytest.raises(TypeError):
+            h.run_kernel("ktile_64x64_w2x2_k128_s3", b, b)
+    finally:
+        h.close()

@@ -18,6 +18,8 @@ LLVM = "/opt/rocm/lib/llvm/bin"
 
 
 def mangled(name):
+    if name.startswith("i8_"):
+        return mangled_i8(name[3:])
     m = re.fullmatch(r"(tile|generic)_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
     if m:
         kind, bm, bn, wm, wn, mf = m.groups()
@@ -47,6 +49,25 @@ def mangled(name):
         return (f"_ZN4mihg13skinny_kernelILi{fm}ELi{fn}ELi{w}ELi{u}ELi{d or 2}"
                 "EEEvNS_8GemmArgsE")
     raise AssertionError(f"unrecognised kernel name {name}")
+
+
+def mangled_i8(name):
+    """Int8 instances: the same tile templates with an i8_ kernel name; the name's
+    K step counts int8 elements (128 per 128-byte LDS row)."""
+    m = re.fullmatch(r"generic_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
+    if m:
+        bm, bn, wm, wn, mf = m.groups()
+        return f"_ZN4mihg17i8_generic_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"d2tile_(\d+)x(\d+)_w(\d+)x(\d+)_m16", name)
+    if m:
+        bm, bn, wm, wn = m.groups()
+        return f"_ZN4mihg16i8_d2tile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)", name)
+    if m:
+        bm, bn, wm, wn, bk, s = m.groups()
+        return (f"_ZN4mihg15i8_ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 128}"
+                f"ELi{s}EEEvNS_8GemmArgsE")
+    raise AssertionError(f"unrecognised int8 kernel name {name}")
 
 
 @pytest.mark.skipif(not (shutil.which("objcopy") and os.path.exists(LLVM + "/llvm-readelf")),
