@@ -7,12 +7,17 @@ resident in HBM), through the library's normal dispatch (or a forced instance wi
 operands rotate over enough copies that every call reads A and B from HBM
 rather than from the 256 MiB MALL ("cold"); ``--warm`` reuses one set.
 
+The int8 variant (int8 operands, exact int32 result) is measured the same way
+with ``--workload i8_square`` or ``i8_llm_MxNxK`` (TOP/s against the int8 MFMA
+peak).
+
 Prints ONE JSON line: throughput (TFLOP/s over the timed steps), the roofline
 of the dominant kernel (its per-launch duration from HIP events recorded on the
 launch stream inside the timed region), and the CPU oracle timed on a bounded
 sample of the same product on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--workload square|tiny|small|llm_MxNxK]
+                    [--workload i8_square|i8_llm_MxNxK]
                     [--mnk M_N_K] [--warm] [--no-cpu-baseline] [--all-configs OUT.jsonl]
                     [--kernel NAME [--group-m G] [--xcd-remap X] [--split-k S]]
 """
@@ -32,7 +37,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "HGEMM TFLOPS and µs/call per (M,N,K) on 1 MI355X; % of roofline"
+METRIC_I8 = "IGEMM (int8 in, int32 out) TOPS and µs/call per (M,N,K) on 1 MI355X; % of roofline"
 PEAK_MFMA_TFLOPS = 2516.6    # dense fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_MFMA_I8_TOPS = 5033.2   # dense int8 MFMA: 256 CU x 2.4 GHz x 8192 OP/clk/CU
 PEAK_HBM_GBS = 8000.0        # HBM3E
 MALL_BYTES = 256 << 20
 
@@ -106,6 +113,11 @@ def problem_for(name, mnk):
         return inputs.Problem(f"mnk_{M}x{N}x{K}", M, N, K, "randn", s, s, 7)
     if name == "square":
         return inputs.square()
+    if name == "i8_square":
+        return inputs.i8_square()
+    for p in inputs.i8_llm():
+        if p.name == name:
+            return p
     if name == "tiny":
         return inputs.tiny()
     if name == "small":
@@ -137,7 +149,8 @@ class Workload:
         for s in range(nsets):
             aa = a if s == 0 else a.clone()
             bb = b if s == 0 else b.clone()
-            cc = torch.empty((p.M, p.N), dtype=torch.float16, device=dev)
+            cc = torch.empty((p.M, p.N), dtype=torch.int32 if p.kind == "i8" else torch.float16,
+                             device=dev)
             self.sets.append((aa, bb, cc))
         torch.cuda.synchronize()
 
@@ -177,9 +190,12 @@ def roofline(p, launch_ms, kernel, workload, raster=(1, 0, 1)):
     flops, nbytes = p.flops, p.min_bytes
     t = launch_ms * 1e-3
     ai = flops / nbytes
-    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    i8 = p.kind == "i8"
+    mfma_peak = PEAK_MFMA_I8_TOPS if i8 else PEAK_MFMA_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai >= ridge:
-        achieved, peak, unit, bound = flops / t / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s", "mfma"
+        achieved, peak, bound = flops / t / 1e12, mfma_peak, "mfma"
+        unit = "TOP/s" if i8 else "TFLOP/s"
     else:
         achieved, peak, unit, bound = nbytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
@@ -193,12 +209,13 @@ def cpu_baseline(p, A, Bt, gpu_c, target_s):
 
     import oracle
     orc = oracle.default()
+    i8 = p.kind == "i8"
 
     def rows(R):
         r = np.repeat(np.arange(R, dtype=np.int64), p.N)
         c = np.tile(np.arange(p.N, dtype=np.int64), R)
         t0 = time.perf_counter()
-        vals = orc.hgemm_tn_entries(A, Bt, r, c)
+        vals = (orc.igemm_tn_entries if i8 else orc.hgemm_tn_entries)(A, Bt, r, c)
         return time.perf_counter() - t0, vals.reshape(R, p.N)
 
     rows(1)                                   # first call starts the oracle's threads
@@ -210,30 +227,48 @@ def cpu_baseline(p, A, Bt, gpu_c, target_s):
         R = max(1, min(p.M, int(R * target_s / max(t, 1e-6))))
         t, vals = rows(R)
     flop = 2.0 * R * p.N * p.K
-    # the sample doubles as a parity check of the timed GPU output
-    g = gpu_c[:R].astype(np.float64)
-    r64 = vals.astype(np.float64)
-    fin = np.isfinite(r64)
-    bound = 1e-3 * np.abs(r64[fin]).max() + 2e-3 * np.abs(r64[fin])
-    ok = bool(np.all(np.abs(g[fin] - r64[fin]) <= bound))
-    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+    # the sample doubles as a parity check of the timed GPU output (exact for int8)
+    if i8:
+        ok = bool(np.array_equal(gpu_c[:R], vals))
+    else:
+        g = gpu_c[:R].astype(np.float64)
+        r64 = vals.astype(np.float64)
+        fin = np.isfinite(r64)
+        bound = 1e-3 * np.abs(r64[fin]).max() + 2e-3 * np.abs(r64[fin])
+        ok = bool(np.all(np.abs(g[fin] - r64[fin]) <= bound))
+    return {"value": round(flop / t / 1e12, 6), "unit": "TOP/s" if i8 else "TFLOP/s",
+            "cores": orc.num_threads(),
             "kind": "oracle", "seconds": round(t, 3),
             "sample": f"rows 0..{R - 1} of C ({R}x{p.N} outputs, K={p.K}) of {p.name}",
             "sample_parity": "ok" if ok else "FAIL"}
 
 
-def torch_matmul_context(wl, steps=20):
-    """torch.matmul (the vendor BLAS) on the same operands, as context only."""
+def torch_call(p):
+    """The vendor library's call for the problem: torch.matmul, or torch._int_mm
+    for int8 (hipBLASLt; it needs M > 16)."""
     import torch
+    if p.kind == "i8":
+        if p.M <= 16:
+            return None
+        return lambda a, b, c: torch._int_mm(a, b.t(), out=c)
+    return lambda a, b, c: torch.matmul(a, b.t(), out=c)
+
+
+def torch_matmul_context(wl, steps=20):
+    """The vendor BLAS on the same operands, as context only."""
+    import torch
+    fn = torch_call(wl.p)
+    if fn is None:
+        return None, None
     a, b, c = wl.sets[0]
     for _ in range(3):
-        torch.matmul(a, b.t(), out=c)
+        fn(a, b, c)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
         a, b, c = wl.sets[i % len(wl.sets)]
-        torch.matmul(a, b.t(), out=c)
+        fn(a, b, c)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -272,7 +307,7 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
     a, b, c = wl.sets[0]
     if force is None:
         kernel, gm, xcd, sk = lib.plan(a, b, c)
-        run = lib.run
+        run = lib.run_i8 if p.kind == "i8" else lib.run
     else:
         kernel, gm, xcd, sk = force
 
@@ -295,11 +330,8 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
         rec["device_us_per_call"] = round(dus, 3)
         rec["device_tflops"] = round(p.flops / (dus * 1e-6) / 1e12, 3)
         rec["device_roofline"] = roofline(p, dus * 1e-3, kernel, p.name, (gm, xcd, sk))
-        if with_torch:
-            import torch
-
-            def tm(a, b, c):
-                torch.matmul(a, b.t(), out=c)
+        tm = torch_call(p) if with_torch else None
+        if tm is not None:
             rec["torch_device_us_per_call"] = round(graph_us(tm, wl, reps), 3)
     return rec, wl
 
@@ -330,8 +362,8 @@ def main():
     if args.all_configs:
         from dense_fp16_gemm_hgemm_amd import inputs
         with open(args.all_configs, "w") as f:
-            for p in inputs.all_named():
-                if p.kind != "randn":
+            for p in inputs.all_named() + inputs.i8_llm() + [inputs.i8_square()]:
+                if p.kind not in ("randn", "i8"):
                     continue
                 for c in (True, False):
                     rec, _ = measure(lib, p, max(20, args.steps // 2), 5, c, with_torch=True,
@@ -339,7 +371,7 @@ def main():
                     f.write(json.dumps(rec) + "\n")
                     f.flush()
                     print(f"# {p.name} {rec['cache']}: device {rec['device_us_per_call']} us "
-                          f"({rec['kernel']} s{rec['split_k']}) torch {rec['torch_device_us_per_call']} us; "
+                          f"({rec['kernel']} s{rec['split_k']}) torch {rec.get('torch_device_us_per_call')} us; "
                           f"stream {rec['us_per_call']} us, torch {rec['torch_matmul_us']} us",
                           file=sys.stderr, flush=True)
                 torch.cuda.empty_cache()
@@ -349,10 +381,11 @@ def main():
     if args.kernel:
         force = (args.kernel, args.group_m, args.xcd_remap, args.split_k)
     rec, wl = measure(lib, p, args.steps, args.warmup, cold, with_torch=True, force=force)
+    i8 = p.kind == "i8"
     out = {
-        "metric": METRIC,
+        "metric": METRIC_I8 if i8 else METRIC,
         "value": rec["tflops"],
-        "unit": "TFLOP/s",
+        "unit": "TOP/s" if i8 else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -360,10 +393,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        "dtype": "int8" if i8 else "fp16",
         "data": "synthetic",
         "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "layout": "TN",
-                   "accumulate": "fp32", "inputs": f"{p.kind} a*{p.a_scale:.6g} b*{p.b_scale:.6g} seed {p.seed}",
+                   "accumulate": "int32" if i8 else "fp32",
+                   "inputs": (f"int8 uniform seed {p.seed}" if i8 else
+                              f"{p.kind} a*{p.a_scale:.6g} b*{p.b_scale:.6g} seed {p.seed}"),
                    "cache": rec["cache"], "operand_sets": rec["sets"], "kernel": rec["kernel"],
                    "group_m": rec["group_m"], "xcd_remap": rec["xcd_remap"],
                    "split_k": rec["split_k"], "dispatch": "forced" if args.kernel else "library",
@@ -371,8 +406,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": rec["roofline"],
         "cpu_baseline": None,
-        "context": {"torch_matmul_tflops": rec["torch_matmul_tflops"],
-                    "torch_matmul_us": rec["torch_matmul_us"],
+        "context": {("torch_int_mm_tops" if i8 else "torch_matmul_tflops"): rec["torch_matmul_tflops"],
+                    ("torch_int_mm_us" if i8 else "torch_matmul_us"): rec["torch_matmul_us"],
                     "source_digest": source_digest()},
     }
     if not args.no_cpu_baseline:

@@ -257,6 +257,8 @@ class Hgemm:
 
     def run(self, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,
             stream=None) -> torch.Tensor:
+        if A.dtype != torch.float16:
+            raise TypeError(f"A must be torch.float16 (int8 operands: run_i8), got {A.dtype}")
         M, N, K, lda, ldb, ldc, out = self._args(A, Bt, out)
         st = mi_hgemm_run(self.handle, M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb,
                           out.data_ptr(), ldc, MI_HGEMM_LAYOUT_TN, _stream_ptr(stream, A.device))
