@@ -11,6 +11,10 @@ The int8 variant (int8 operands, exact int32 result) is measured the same way
 with ``--workload i8_square`` or ``i8_llm_MxNxK`` (TOP/s against the int8 MFMA
 peak).
 
+``--server`` measures the server mode instead (requests of the tiny problem
+arriving at a target QPS, and the highest rate sustained), with the native load
+generator ``mi_hgemm_serve`` against rocBLAS on the same operands.
+
 Prints ONE JSON line: throughput (TFLOP/s over the timed steps), the roofline
 of the dominant kernel (its per-launch duration from HIP events recorded on the
 launch stream inside the timed region), and the CPU oracle timed on a bounded
@@ -62,6 +66,9 @@ def parse():
     ap.add_argument("--group-m", type=int, default=1, help="raster group height with --kernel")
     ap.add_argument("--xcd-remap", type=int, default=0, choices=(0, 1), help="XCD remap with --kernel")
     ap.add_argument("--split-k", type=int, default=1, help="K split with --kernel")
+    ap.add_argument("--server", action="store_true",
+                    help="server-mode QPS of the tiny problem (64, 4096, 64) instead")
+    ap.add_argument("--target-qps", type=float, default=100.0, help="arrival rate with --server")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (to scale "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -336,12 +343,84 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
     return rec, wl
 
 
+def server_cpu_baseline(mnk, target_s):
+    """The oracle serving requests of the same problem back to back on the host
+    cores: requests per second over ~target_s."""
+    import numpy as np
+
+    import oracle
+    from dense_fp16_gemm_hgemm_amd import inputs
+    orc = oracle.default()
+    M, N, K = (int(x) for x in mnk.split("_"))
+    A, Bt = inputs.make(inputs.Problem("server", M, N, K, "randn", 1 / math.sqrt(K),
+                                       1 / math.sqrt(K), 1))
+    orc.hgemm_tn(A, Bt)                                   # starts the oracle's threads
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        orc.hgemm_tn(A, Bt)
+        n += 1
+    t = time.perf_counter() - t0
+    return {"value": round(n / t, 3), "unit": "requests/s", "cores": orc.num_threads(),
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"{n} requests of {M}x{N}x{K}, served back to back"}
+
+
+def server_main(args):
+    """Server mode: Poisson arrivals at the target rate, and the highest
+    sustained rate (back to back, 8 in flight), for the library and rocBLAS.
+    Runs the load generator as a child process before this process touches the
+    GPU."""
+    from dense_fp16_gemm_hgemm_amd import server_mode
+    mnk = args.mnk or "64_4096_64"
+    runs = {}
+    for backend in ("mi_hgemm", "rocblas"):
+        runs[backend] = {
+            "target": server_mode.run(mnk, "poisson", args.target_qps,
+                                      requests=max(50, int(args.target_qps * 5)), backend=backend),
+            "saturation": server_mode.run(mnk, "closed", requests=max(args.steps, 1) * 200,
+                                          depth=8, backend=backend),
+        }
+    ours, vend = runs["mi_hgemm"], runs["rocblas"]
+    sat = ours["saturation"]["achieved_qps"]
+    # both at 80% of our sustained rate: latency under a heavy but stable load
+    for backend in ("mi_hgemm", "rocblas"):
+        runs[backend]["load80"] = server_mode.run(mnk, "poisson", 0.8 * sat, requests=20000,
+                                                  backend=backend)
+    M, N, K = (int(x) for x in mnk.split("_"))
+    out = {
+        "metric": "server-mode QPS of the (64,4096,64) HGEMM on 1 MI355X (sustained, 8 in flight)",
+        "value": round(sat, 1),
+        "unit": "requests/s",
+        "n_gpus": 1,
+        "steps": max(args.steps, 1) * 200,
+        "warmup": 64,
+        "ms_per_step": round(1e3 / sat, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": f"server_{M}x{N}x{K}", "M": M, "N": N, "K": K,
+                   "target_qps": args.target_qps, "dispatch": "library",
+                   "parallelism": "none (1 GPU)"},
+        "server": runs,
+        "context": {"rocblas_sustained_qps": vend["saturation"]["achieved_qps"],
+                    "ours_over_rocblas": round(sat / vend["saturation"]["achieved_qps"], 3)},
+        "roofline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else server_cpu_baseline(mnk, args.cpu_seconds),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
+    if args.server:
+        server_main(args)
+        return
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
