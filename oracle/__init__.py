@@ -16,6 +16,11 @@ B ("TN").  With B column-major K x N, its storage is N rows of K halves, i.e. th
 stored as int32 (the INT8 mode of the same page's 正文 paragraph 3; the page
 leaves the result type open and the exact int32 sum is the reading taken).
 
+``fma_chain`` is the arithmetic of the load/compute overlap micro-benchmark:
+every element after ``fma_iters`` steps of ``y = fmaf(y, alpha, beta)``, one
+binary32 rounding per step ("B-08. Hopper TMA：从单线程 Bulk Copy 到吞吐墙"
+(lqnn.cn) §5, the FMA-iterations intensity knob).
+
 Parity pins for every function here live in ``tests/test_oracle_pins.py``; no
 function of the oracle is unpinned.
 """
@@ -89,6 +94,8 @@ class Oracle:
         lib.ref_igemm_tn.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
         lib.ref_igemm_tn_entries.restype = ctypes.c_int
         lib.ref_igemm_tn_entries.argtypes = [i64, i64, i64, p, i64, p, i64, i64, p, p, p]
+        lib.ref_fma_chain.restype = ctypes.c_int
+        lib.ref_fma_chain.argtypes = [p, p, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_float]
         lib.ref_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -213,6 +220,16 @@ class Oracle:
             raise ValueError("oracle rejected the arguments")
         return out
 
+    def fma_chain(self, x: np.ndarray, fma_iters: int, alpha: float, beta: float) -> np.ndarray:
+        """Each element after ``fma_iters`` steps of y = fmaf(y, alpha, beta) (binary32)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty_like(x)
+        rc = self.lib.ref_fma_chain(x.ctypes.data, out.ctypes.data, x.size, int(fma_iters),
+                                    float(alpha), float(beta))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.ref_num_threads())
@@ -250,6 +267,10 @@ def igemm_tn(A, Bt, C=None):
 
 def igemm_tn_entries(A, Bt, rows, cols):
     return default().igemm_tn_entries(A, Bt, rows, cols)
+
+
+def fma_chain(x, fma_iters, alpha, beta):
+    return default().fma_chain(x, fma_iters, alpha, beta)
 
 
 def num_threads():

@@ -43,6 +43,11 @@
  * over int8 operands, stored as int32 (a sum that does not fit int32 is
  * reported, not wrapped).
  *
+ * The overlap micro-benchmark's arithmetic (ref_fma_chain): "B-08. Hopper TMA：
+ * 从单线程 Bulk Copy 到吞吐墙" (lqnn.cn) §5 sweeps a number of FMA iterations per
+ * loaded element; here each element becomes y = x, then fma_iters times
+ * y = fmaf(y, alpha, beta), with C99 fmaf (one rounding to binary32 per step).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (see oracle/__init__.py).
  */
 #include <math.h>
@@ -224,6 +229,22 @@ int ref_igemm_tn_entries(int64_t M, int64_t N, int64_t K,
         else bad = 1;
     }
     return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------ overlap arithmetic -- */
+
+/* out[i] = x[i] after fma_iters steps of y = fmaf(y, alpha, beta). */
+int ref_fma_chain(const float* x, float* out, int64_t n, int32_t fma_iters, float alpha,
+                  float beta)
+{
+    if (n < 0 || fma_iters < 0) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float y = x[i];
+        for (int32_t it = 0; it < fma_iters; ++it) y = fmaf(y, alpha, beta);
+        out[i] = y;
+    }
+    return 0;
 }
 
 /* Threads an OpenMP parallel region of this library uses. */

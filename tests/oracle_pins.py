@@ -412,11 +412,70 @@ def pin_i8_strides_entries_empty(orc):
                           np.zeros((4, 6), np.int32)), "K = 0"
 
 
+# ------------------------------------------------- overlap micro-benchmark --
+
+def exact_to_f32(q: Fraction) -> float:
+    """Round an exact rational to binary32, ties to even (IEEE 754 binary32),
+    normal range only (the pins below stay there)."""
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert -126 <= e <= 127, "outside the normal binary32 range"
+    scaled = a / Fraction(2) ** (e - 23)          # in [2^23, 2^24)
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return sign * float(Fraction(m) * Fraction(2) ** (e - 23))
+
+
+def pin_fma_chain_bruteforce(orc):
+    """Random binary32 inputs, constants and step counts: each step is the exact
+    product-plus-addend rounded once to binary32 (a fused multiply-add)."""
+    rng = np.random.default_rng(31)
+    fused_differs = False
+    for trial in range(40):
+        x = (rng.uniform(-1, 1, 16) * 2.0 ** rng.integers(-8, 8, 16)).astype(np.float32)
+        alpha = np.float32(rng.uniform(0.5, 1.5))
+        beta = np.float32(rng.uniform(-1, 1))
+        iters = int(rng.integers(1, 9))
+        got = orc.fma_chain(x, iters, float(alpha), float(beta))
+        for i in range(x.size):
+            y = float(x[i])
+            for _ in range(iters):
+                y = exact_to_f32(Fraction(y) * Fraction(float(alpha)) + Fraction(float(beta)))
+            assert float(got[i]) == y, f"trial {trial} element {i}: {got[i]!r} vs exact {y!r}"
+            # the same steps with two roundings (multiply, then add) differ somewhere
+            z = np.float32(x[i])
+            for _ in range(iters):
+                z = np.float32(np.float32(z * alpha) + beta)
+            fused_differs |= bool(z != np.float32(y))
+    assert fused_differs, "no case separates fused from unfused steps; the pin is too weak"
+
+
+def pin_fma_chain_closed_forms(orc):
+    """Zero steps and (alpha, beta) = (1, 0) leave x unchanged; (2, 0) multiplies
+    by 2^k exactly; (0.5, 0.25) on dyadic inputs is exact: y_k = x/2^k + (1 - 2^-k)/2."""
+    rng = np.random.default_rng(32)
+    x = rng.uniform(-4, 4, 1000).astype(np.float32)
+    assert np.array_equal(orc.fma_chain(x, 0, 0.3, 0.7).view(np.uint32), x.view(np.uint32))
+    assert np.array_equal(orc.fma_chain(x, 17, 1.0, 0.0).view(np.uint32), x.view(np.uint32))
+    assert np.array_equal(orc.fma_chain(x, 5, 2.0, 0.0), x * np.float32(32.0))
+    xd = (rng.integers(-1024, 1024, 1000) / 256.0).astype(np.float32)
+    for k in (1, 3, 6):
+        want = xd.astype(np.float64) / 2 ** k + (1 - 2.0 ** -k) / 2
+        assert np.array_equal(orc.fma_chain(xd, k, 0.5, 0.25).astype(np.float64), want), k
+
+
 ALL_PINS = [
     pin_decode_exhaustive, pin_encode_exhaustive, pin_encoding_golden,
     pin_handworked_golden, pin_bruteforce_fraction, pin_identity, pin_identity_right,
     pin_permutation, pin_small_integer, pin_numpy_crosscheck, pin_metamorphic,
     pin_strides, pin_entries, pin_empty,
     pin_i8_bruteforce, pin_i8_closed_forms, pin_i8_int32_limit, pin_i8_numpy_and_metamorphic,
-    pin_i8_strides_entries_empty,
+    pin_i8_strides_entries_empty, pin_fma_chain_bruteforce, pin_fma_chain_closed_forms,
 ]

@@ -43,6 +43,11 @@ MUTANTS = {
     "i8_ldc_ignored": ("if (fits_int32(s)) C[i * ldc + j]", "if (fits_int32(s)) C[i * N + j]"),
     "i8_transposed": ("const int64_t s = idot(A + i * lda, B + j * ldb, K);",
                       "const int64_t s = idot(A + (j % M) * lda, B + (i % N) * ldb, K);"),
+    # overlap micro-benchmark arithmetic
+    "fma_unfused": ("y = fmaf(y, alpha, beta);", "y = (float)(y * alpha) + beta;"),
+    "fma_one_step_short": ("for (int32_t it = 0; it < fma_iters; ++it)",
+                           "for (int32_t it = 1; it < fma_iters; ++it)"),
+    "fma_operands_swapped": ("y = fmaf(y, alpha, beta);", "y = fmaf(y, beta, alpha);"),
     "i8_ldb_ignored": ("const int64_t s = idot(A + rows[t] * lda, B + cols[t] * ldb, K);",
                        "const int64_t s = idot(A + rows[t] * lda, B + cols[t] * K, K);"),
 }
