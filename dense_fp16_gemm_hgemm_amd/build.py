@@ -5,7 +5,9 @@ Every ``csrc/*.hip`` file is compiled for ``--offload-arch=gfx950`` and every
 linked into ``dense_fp16_gemm_hgemm_amd/libmi_hgemm.so``.  Packed fp32 VALU
 instructions are disabled for all device code.
 
-It also builds ``dense_fp16_gemm_hgemm_amd/mi_hgemm_serve``, the server-mode
+It also builds ``dense_fp16_gemm_hgemm_amd/libmi_overlap.so`` (the load/compute
+overlap micro-benchmark, ``overlap/overlap.hip``) and
+``dense_fp16_gemm_hgemm_amd/mi_hgemm_serve``, the server-mode
 load generator (``serve/serve_bench.cpp``), linked against the library (found
 beside it at run time) and rocBLAS (the vendor backend it compares with).
 
@@ -24,6 +26,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmi_hgemm.so")
+OVERLAP_SRC = os.path.join(PKG, "overlap", "overlap.hip")
+OVERLAP_PATH = os.path.join(PKG, "libmi_overlap.so")
 SERVE_SRC = os.path.join(PKG, "serve", "serve_bench.cpp")
 SERVE_PATH = os.path.join(PKG, "mi_hgemm_serve")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -79,6 +83,13 @@ def build(verbose: bool = False) -> str:
             *[obj for _, obj, _ in cmds], "-ldl"]
     subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
+    tmp = OVERLAP_PATH + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, *COMMON, *DEVICE, "-shared", OVERLAP_SRC, "-o", tmp],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for " + OVERLAP_SRC)
+    os.replace(tmp, OVERLAP_PATH)
     tmp = SERVE_PATH + ".tmp%d" % os.getpid()
     serve = [HIPCC, *COMMON, *DEVICE, "-x", "hip", SERVE_SRC, "-x", "none", "-o", tmp,
              "-L", PKG, "-lmi_hgemm", "-L/opt/rocm/lib", "-lrocblas",
