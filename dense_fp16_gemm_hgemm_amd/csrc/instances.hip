@@ -51,6 +51,11 @@ namespace mihg {
   X(64, 128, 2, 2)                \
   X(64, 64, 2, 2)
 
+// D2TILE3: X(BM, BN, WGM, WGN): d2tile with three A stages (A copied two trips ahead)
+#define MIHG_D2TILE3_INSTANCES(X) \
+  X(256, 256, 2, 4)               \
+  X(256, 256, 2, 2)
+
 // PPTILE: X(BM, BN): eight waves in two ping-pong groups
 #define MIHG_PPTILE_INSTANCES(X) \
   X(256, 256)                    \
@@ -62,6 +67,9 @@ namespace mihg {
   X(256, 256, 2, 4)                 \
   X(256, 128, 2, 2)                 \
   X(128, 128, 2, 2)
+
+#define MIHG_I8_D2TILE3_INSTANCES(X) \
+  X(256, 256, 2, 4)
 
 #define MIHG_I8_KTILE_INSTANCES(X) \
   X(128, 128, 2, 4, 256, 2)        \
@@ -113,6 +121,10 @@ namespace mihg {
   template __global__ void dtile_kernel<BM, BN, WGM, WGN, MF, S>(GemmArgs);
 #define INSTANTIATE_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_D2TILE3(BM, BN, WGM, WGN) \
+  template __global__ void d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_I8_D2TILE3(BM, BN, WGM, WGN) \
+  template __global__ void i8_d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
@@ -126,11 +138,13 @@ template __global__ void generic_kernel<64, 64, 2, 2, 32>(GemmArgs);
 MIHG_TILE_INSTANCES(INSTANTIATE_TILE)
 MIHG_DTILE_INSTANCES(INSTANTIATE_DTILE)
 MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
+MIHG_D2TILE3_INSTANCES(INSTANTIATE_D2TILE3)
 MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
 MIHG_I8_D2TILE_INSTANCES(INSTANTIATE_I8_D2TILE)
+MIHG_I8_D2TILE3_INSTANCES(INSTANTIATE_I8_D2TILE3)
 MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 
 // The registry holds host launch functions, so it exists only in the host pass.
@@ -146,6 +160,13 @@ MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
    1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+#define D2TILE3_DESC(BM, BN, WGM, WGN)                                                     \
+  {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
+   1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+#define I8_D2TILE3_DESC(BM, BN, WGM, WGN)                                                    \
+  {"i8_d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN,   \
+   16, 1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_i8_d2tile3<BM, BN, WGM, WGN>,          \
+   &grid_tile<BM, BN>, DTYPE_I8},
 #define PPTILE_DESC(BM, BN)                                                                \
   {"pptile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                     \
    2 * (BM + BN) * kD2Row * 2, 0, &launch_pptile<BM, BN>, &grid_tile<BM, BN>},
@@ -172,6 +193,7 @@ const KernelDesc kKernels[] = {
     MIHG_TILE_INSTANCES(TILE_DESC)
     MIHG_DTILE_INSTANCES(DTILE_DESC)
     MIHG_D2TILE_INSTANCES(D2TILE_DESC)
+    MIHG_D2TILE3_INSTANCES(D2TILE3_DESC)
     MIHG_PPTILE_INSTANCES(PPTILE_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
@@ -179,6 +201,7 @@ const KernelDesc kKernels[] = {
     {"i8_generic_64x64_w2x2_m16", FAMILY_TILE, 64, 64, 128, 4, 16, 0, 1, 128 * 64 * 2, 0,
      &launch_i8_generic<64, 64, 2, 2, 16>, &grid_tile<64, 64>, DTYPE_I8},
     MIHG_I8_D2TILE_INSTANCES(I8_D2TILE_DESC)
+    MIHG_I8_D2TILE3_INSTANCES(I8_D2TILE3_DESC)
     MIHG_I8_KTILE_INSTANCES(I8_KTILE_DESC)
 };
 

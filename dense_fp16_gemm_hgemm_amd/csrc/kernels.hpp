@@ -856,7 +856,7 @@ dtile_kernel(GemmArgs p) {
 // rows; its lanes need one of two global offsets (even or odd block).
 constexpr int kD2Row = 64;  // halves per LDS row
 
-template <typename Op, int BM, int BN, int WGM, int WGN>
+template <typename Op, int BM, int BN, int WGM, int WGN, int SA>
 __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<16>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -868,11 +868,20 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   constexpr int A_BLK = BM / 8 / NW, B_BLK = BN / 8 / NW;  // 1 KiB copies per wave
   constexpr int ND = A_BLK + B_BLK;
   constexpr int STAGE = (BM + BN) * kD2Row;
+  // LDS: SA stages of A and 2 of B.  SA = 2: stage s holds A then B rows at
+  // s * STAGE.  SA = 3: the A ring (3 x BM rows) and then the B ring (2 x BN
+  // rows).
+  constexpr int A_STRIDE = SA == 2 ? STAGE : BM * kD2Row;
+  constexpr int B_OFF = SA == 2 ? BM * kD2Row : SA * BM * kD2Row;
+  constexpr int B_STRIDE = SA == 2 ? STAGE : BN * kD2Row;
+  constexpr int LDS_HALVES = SA == 2 ? 2 * STAGE : SA * BM * kD2Row + 2 * BN * kD2Row;
+  static_assert(SA == 2 || SA == 3, "two or three A stages");
+  static_assert(LDS_HALVES * 2 <= 160 * 1024, "LDS budget");
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "copy blocks must split evenly");
   static_assert(A_BLK % 2 == 0 && B_BLK % 2 == 0, "blocks pair up by parity");
 
-  __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[LDS_HALVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -895,23 +904,32 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   const uint32_t b_v0 = (uint32_t)(drow * ldb * EB + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * EB + dch1 * 16);
   const bool mask_k = (K % BK) != 0;
   const uint32_t lds0 = lds_addr(lds);
-  // copy x (0..ND-1) of tile k0 into stage st
-  auto dma_one = [&](int st, int k0, int x) {
-    const uint32_t kb = (uint32_t)k0 * EB;
-    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
-    if (x < A_BLK) {
-      const int blk = wave_u * A_BLK + x;
-      const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (k0 + ch * EPC < K);
-      dma16(rda, kin ? ((x & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * EB) + kb,
-            sbase + blk * 8 * kD2Row * 2);
+  // copy x (0..ND-1): A block xa of tile ka into A stage ast, or B block xb of
+  // tile kb into B stage bst.  SA = 2 issues A's blocks first, SA = 3 B's
+  // (the B copies must land this trip, A's only the next).
+  auto dma_a = [&](int ast, int k0, int xa) {
+    const uint32_t kbytes = (uint32_t)k0 * EB;
+    const int blk = wave_u * A_BLK + xa;
+    const int ch = (xa & 1) ? dch1 : dch0;
+    const bool kin = !mask_k || (k0 + ch * EPC < K);
+    dma16(rda, kin ? ((xa & 1) ? a_v1 : a_v0) : kOOB, (uint32_t)(blk * 8 * lda * EB) + kbytes,
+          lds0 + (uint32_t)((ast * A_STRIDE + blk * 8 * kD2Row) * 2));
+  };
+  auto dma_b = [&](int bst, int k0, int xb) {
+    const uint32_t kbytes = (uint32_t)k0 * EB;
+    const int blk = wave_u * B_BLK + xb;
+    const int ch = (xb & 1) ? dch1 : dch0;
+    const bool kin = !mask_k || (k0 + ch * EPC < K);
+    dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * EB) + kbytes,
+          lds0 + (uint32_t)((B_OFF + bst * B_STRIDE + blk * 8 * kD2Row) * 2));
+  };
+  auto dma_one = [&](int ast, int bst, int ka, int kb, int x) {
+    if constexpr (SA == 2) {
+      if (x < A_BLK) dma_a(ast, ka, x);
+      else dma_b(bst, kb, x - A_BLK);
     } else {
-      const int xb = x - A_BLK;
-      const int blk = wave_u * B_BLK + xb;
-      const int ch = (xb & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (k0 + ch * EPC < K);
-      dma16(rdb, kin ? ((xb & 1) ? b_v1 : b_v0) : kOOB, (uint32_t)(blk * 8 * ldb * EB) + kb,
-            sbase + (BM + blk * 8) * kD2Row * 2);
+      if (x < B_BLK) dma_b(bst, kb, x);
+      else dma_a(ast, ka, x - B_BLK);
     }
   };
 
@@ -925,12 +943,12 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     fb_off[s] = (BM + wn * WTN + frow) * kD2Row + phys * 8;
   }
   h8 fa[2][FM], fb[2][FN];  // [step]
-  auto fread_one = [&](int st, int s, int r) {
-    const _Float16* base = lds + st * STAGE;
+  auto fread_one = [&](int ast, int bst, int s, int r) {
     if (r < FM)
-      fa[s][r] = *reinterpret_cast<const h8*>(base + fa_off[s] + r * MF * kD2Row);
+      fa[s][r] = *reinterpret_cast<const h8*>(lds + ast * A_STRIDE + fa_off[s] + r * MF * kD2Row);
     else
-      fb[s][r - FM] = *reinterpret_cast<const h8*>(base + fb_off[s] + (r - FM) * MF * kD2Row);
+      fb[s][r - FM] = *reinterpret_cast<const h8*>(lds + B_OFF - BM * kD2Row + bst * B_STRIDE +
+                                                   fb_off[s] + (r - FM) * MF * kD2Row);
   };
 
   typename MM::acc_t acc[FM][FN];
@@ -948,7 +966,8 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // while copies last.  (Spreading them over the whole half measured ~1.5%
   // faster on 8192^3 than packing them into its first three quarters, and
   // issuing every copy first was ~3% slower.)
-  auto half = [&](auto DO_MFMA, auto COPY, auto S_MFMA, auto S_READ, int rst, int kcopy, int wst) {
+  auto half = [&](auto DO_MFMA, auto COPY, auto S_MFMA, auto S_READ, int rast, int rbst, int ka,
+                  int kb, int wast, int wbst) {
     constexpr int SPAN = NM;
     constexpr int nd = decltype(COPY)::value ? ND : 0;
     constexpr int nx = nd + NR;
@@ -963,12 +982,12 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
       for (int x = 0; x < nx; ++x) {
         if (x * SPAN / nx != i) continue;
         if (x < 2 * npair) {
-          if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
-          else fread_one(rst, sr, x / 2);
+          if (x % 2 == 0) dma_one(wast, wbst, ka, kb, x / 2);
+          else fread_one(rast, rbst, sr, x / 2);
         } else if (nd > NR) {
-          dma_one(wst, kcopy, x - npair);
+          dma_one(wast, wbst, ka, kb, x - npair);
         } else {
-          fread_one(rst, sr, x - npair);
+          fread_one(rast, rbst, sr, x - npair);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -980,12 +999,26 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto wait_all = [&]() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8)); };  // vmcnt(0)
+  // vmcnt(A_BLK): all but this wave's last A_BLK copies have landed
+  auto wait_but_a = [&]() {
+    constexpr int n = A_BLK;
+    static_assert(n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  };
 
   const int nk = (K + BK - 1) / BK;
-  // prologue: tile 0 in stage 0
+  // prologue: tile 0 in stage 0 (and, with SA = 3, A of tile 1 in A stage 1)
 #pragma unroll
-  for (int x = 0; x < ND; ++x) dma_one(0, 0, x);
-  wait_all();
+  for (int x = 0; x < A_BLK; ++x) dma_a(0, 0, x);
+#pragma unroll
+  for (int x = 0; x < B_BLK; ++x) dma_b(0, 0, x);
+  if constexpr (SA == 3) {
+#pragma unroll
+    for (int x = 0; x < A_BLK; ++x) dma_a(1, BK, x);
+    wait_but_a();
+  } else {
+    wait_all();
+  }
   __syncthreads();
   // Trip 0 runs the same body: its "step 1 of the previous tile" MFMAs use
   // zeroed fragments and add exactly 0.
@@ -994,12 +1027,16 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // first half: step 1 of tile kt-1, copies of tile kt+1, step-0 fragments of tile kt
-    half(T{}, T{}, I1{}, I0{}, st, (kt + 1) * BK, st ^ 1);
+    // tile kt is in A stage kt % SA and B stage kt % 2; this trip copies B of
+    // tile kt+1 and A of tile kt+SA-1 into the stages tile kt-1 left
+    const int ast = SA == 2 ? (kt & 1) : kt % 3, bst = kt & 1;
+    const int wast = SA == 2 ? (ast ^ 1) : (ast == 0 ? 2 : ast - 1);
+    // first half: step 1 of tile kt-1, the copies, step-0 fragments of tile kt
+    half(T{}, T{}, I1{}, I0{}, ast, bst, (kt + SA - 1) * BK, (kt + 1) * BK, wast, bst ^ 1);
     // second half: step 0 of tile kt, step-1 fragments of tile kt
-    half(T{}, F{}, I0{}, I1{}, st, 0, 0);
-    wait_all();
+    half(T{}, F{}, I0{}, I1{}, ast, bst, 0, 0, 0, 0);
+    if constexpr (SA == 3) wait_but_a();  // tile kt+1 has landed; A of kt+2 may fly
+    else wait_all();
     __syncthreads();
   }
   // the last tile's step 1 (its fragments were read in the last trip)
@@ -1007,6 +1044,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+  if constexpr (SA == 3) wait_all();  // A copies past the last tile drain before exit
 
   char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
@@ -1037,12 +1075,22 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
 
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN) d2tile_kernel(GemmArgs p) {
-  d2tile_body<OpF16, BM, BN, WGM, WGN>(p);
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 2>(p);
 }
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile_kernel(GemmArgs p) {
-  d2tile_body<OpI8, BM, BN, WGM, WGN>(p);
+  d2tile_body<OpI8, BM, BN, WGM, WGN, 2>(p);
 }
+// Three A stages: A's copies are issued two trips ahead, B's one.
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tile3_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 3>(p);
+}
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile3_kernel(GemmArgs p) {
+  d2tile_body<OpI8, BM, BN, WGM, WGN, 3>(p);
+}
+
 
 // ---------------------------------------------------------------------------
 // Ping-pong family ("pptile"): BM x BN x 64 tiles, 8 waves in two groups of
@@ -1817,6 +1865,22 @@ template <int BM, int BN, int WGM, int WGN, int MF>
 hipError_t launch_generic(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((generic_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_d2tile3(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((d2tile3_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g), dim3(64 * WGM * WGN),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_i8_d2tile3(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((i8_d2tile3_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
