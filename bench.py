@@ -79,12 +79,20 @@ def parse():
 DEVICE_SOURCES = ("kernels.hpp", "instances.hip", "internal.h")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (comments do not change the kernels)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for name in DEVICE_SOURCES:
-        with open(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", name), "rb") as fh:
+        with open(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", name), encoding="utf-8") as fh:
             h.update(name.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -854,6 +854,15 @@ dtile_kernel(GemmArgs p) {
 // 16 consecutive rows read at one logical chunk fall on 16 distinct (row
 // parity, chunk) bank groups of a 64-bank LDS.  A copy instruction fills 8
 // rows; its lanes need one of two global offsets (even or odd block).
+//
+// With one tile of copies in flight the global -> LDS copy path is bound by
+// its latency, not its bandwidth (a 256 x 256 tile's copies alone run about
+// 1.4x faster with two tiles in flight), but 160 KiB of LDS holds only 2.5
+// stages of a 256 x 256 x 64 tile.  The SA = 3 form ("d2tile3") gives the
+// spare half stage to A: A has three stages and is copied two trips ahead, B
+// has two and is copied one trip ahead.  B's copies are issued first, so the
+// wait at the end of a trip leaves exactly the A copies of this trip in
+// flight (vmcnt counts this wave's copies in issue order).
 constexpr int kD2Row = 64;  // halves per LDS row
 
 template <typename Op, int BM, int BN, int WGM, int WGN, int SA>
