@@ -51,10 +51,13 @@ namespace mihg {
   X(64, 128, 2, 2)                \
   X(64, 64, 2, 2)
 
-// D2TILE3: X(BM, BN, WGM, WGN): d2tile with three A stages (A copied two trips ahead)
+// D2TILE3: X(BM, BN, WGM, WGN, MF): d2tile with three A stages (A copied two
+// trips ahead), MFMA 16x16x32 or 32x32x16
 #define MIHG_D2TILE3_INSTANCES(X) \
-  X(256, 256, 2, 4)               \
-  X(256, 256, 2, 2)
+  X(256, 256, 2, 4, 16)           \
+  X(256, 256, 2, 2, 16)           \
+  X(256, 256, 2, 4, 32)           \
+  X(256, 256, 2, 2, 32)
 
 // PPTILE: X(BM, BN): eight waves in two ping-pong groups
 #define MIHG_PPTILE_INSTANCES(X) \
@@ -121,8 +124,8 @@ namespace mihg {
   template __global__ void dtile_kernel<BM, BN, WGM, WGN, MF, S>(GemmArgs);
 #define INSTANTIATE_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
-#define INSTANTIATE_D2TILE3(BM, BN, WGM, WGN) \
-  template __global__ void d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_D2TILE3(BM, BN, WGM, WGN, MF) \
+  template __global__ void d2tile3_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
 #define INSTANTIATE_I8_D2TILE3(BM, BN, WGM, WGN) \
   template __global__ void i8_d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
@@ -160,9 +163,10 @@ MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 #define D2TILE_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
    1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tile<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
-#define D2TILE3_DESC(BM, BN, WGM, WGN)                                                     \
-  {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16, 1, \
-   1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
+#define D2TILE3_DESC(BM, BN, WGM, WGN, MF)                                                  \
+  {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, \
+   1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3<BM, BN, WGM, WGN, MF>,              \
+   &grid_tile<BM, BN>},
 #define I8_D2TILE3_DESC(BM, BN, WGM, WGN)                                                    \
   {"i8_d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN,   \
    16, 1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_i8_d2tile3<BM, BN, WGM, WGN>,          \

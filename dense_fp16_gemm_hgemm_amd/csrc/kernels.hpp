@@ -167,6 +167,7 @@ struct OpF16 {
   static constexpr int kCB = 2;  // result bytes per element
   typedef _Float16 in_t;
   typedef _Float16 out_t;
+  typedef f32x4 acc4_t;  // four accumulators of one output row
   template <int MF>
   using Mma = Mfma<MF>;
   // four consecutive results of one output row, at byte offset off
@@ -186,6 +187,7 @@ struct OpI8 {
   static constexpr int kCB = 4;
   typedef int8_t in_t;
   typedef int32_t out_t;
+  typedef i32x4 acc4_t;
   template <int MF>
   using Mma = MfmaI8;
   __device__ static inline void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4 v) {
@@ -865,12 +867,16 @@ dtile_kernel(GemmArgs p) {
 // flight (vmcnt counts this wave's copies in issue order).
 constexpr int kD2Row = 64;  // halves per LDS row
 
-template <typename Op, int BM, int BN, int WGM, int WGN, int SA>
+template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16>
 __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
-  using MM = typename Op::template Mma<16>;
+  using MM = typename Op::template Mma<MF>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
-  constexpr int MF = 16, BK = 128 / EB, KSTEPS = 2;  // BK: elements per 128-byte LDS row
-  constexpr int EPC = 16 / EB;                         // elements per 16-byte chunk
+  constexpr int BK = 128 / EB;      // elements per 128-byte LDS row
+  constexpr int EPC = 16 / EB;      // elements per 16-byte chunk
+  constexpr int KSTEPS = BK / MM::KI;  // MFMA k-steps per K tile (2 for MF 16, 4 for MF 32)
+  constexpr int SPH = KSTEPS / 2;      // k-steps per half trip
+  constexpr int CPS = MM::KI / EPC;    // 16-byte chunks per k-step
+  static_assert(MF == 16 || (MF == 32 && EB == 2), "32x32 MFMAs for binary16 only");
   constexpr int NT = 64 * WGM * WGN, NW = NT / 64;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int FM = WTM / MF, FN = WTN / MF;
@@ -942,22 +948,26 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     }
   };
 
-  // fragments: row base + per-lane physical chunk of logical chunk 4s + l/16
+  // fragments of k-step t: row base + per-lane physical chunk of logical
+  // chunk CPS*t + l/MF (rows are multiples of MF plus l % MF, so the swizzle
+  // term is ((l % MF) >> 1) & 7; 16 lanes read 16 consecutive rows per pass)
   const int frow = lane % MF, fq = lane / MF, fsw = (frow >> 1) & 7;
   int fa_off[KSTEPS], fb_off[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    const int phys = (4 * s + fq) ^ fsw;
+    const int phys = (CPS * s + fq) ^ fsw;
     fa_off[s] = (wm * WTM + frow) * kD2Row + phys * 8;
     fb_off[s] = (BM + wn * WTN + frow) * kD2Row + phys * 8;
   }
-  h8 fa[2][FM], fb[2][FN];  // [step]
-  auto fread_one = [&](int ast, int bst, int s, int r) {
-    if (r < FM)
-      fa[s][r] = *reinterpret_cast<const h8*>(lds + ast * A_STRIDE + fa_off[s] + r * MF * kD2Row);
+  h8 fa[2][SPH][FM], fb[2][SPH][FN];  // [half][k-step within the half]
+  // read r of half h: k-step h*SPH + r / (FM + FN), A's fragments then B's
+  auto fread_one = [&](int ast, int bst, int h, int r) {
+    const int u = r / (FM + FN), q = r % (FM + FN), s = h * SPH + u;
+    if (q < FM)
+      fa[h][u][q] = *reinterpret_cast<const h8*>(lds + ast * A_STRIDE + fa_off[s] + q * MF * kD2Row);
     else
-      fb[s][r - FM] = *reinterpret_cast<const h8*>(lds + B_OFF - BM * kD2Row + bst * B_STRIDE +
-                                                   fb_off[s] + (r - FM) * MF * kD2Row);
+      fb[h][u][q - FM] = *reinterpret_cast<const h8*>(lds + B_OFF - BM * kD2Row + bst * B_STRIDE +
+                                                      fb_off[s] + (q - FM) * MF * kD2Row);
   };
 
   typename MM::acc_t acc[FM][FN];
@@ -968,7 +978,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
 #pragma unroll
       for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0;
 
-  constexpr int NM = FM * FN, NR = FM + FN;
+  constexpr int NM = SPH * FM * FN, NR = SPH * (FM + FN);  // per half
   // One half trip: the NM MFMAs of step S_MFMA (when DO_MFMA), with the
   // copies of the next tile (when COPY) and the NR fragment reads of step
   // S_READ spread evenly over its MFMA slots; copies and reads alternate
@@ -984,9 +994,9 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     constexpr int sm = decltype(S_MFMA)::value, sr = decltype(S_READ)::value;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      const int fm = i / FN, fn = i % FN;
+      const int u = i / (FM * FN), fm = (i % (FM * FN)) / FN, fn = i % FN;
       if constexpr (decltype(DO_MFMA)::value)
-        acc[fm][fn] = MM::mma(fb[sm][fn], fa[sm][fm], acc[fm][fn]);
+        acc[fm][fn] = MM::mma(fb[sm][u][fn], fa[sm][u][fm], acc[fm][fn]);
 #pragma unroll
       for (int x = 0; x < nx; ++x) {
         if (x * SPAN / nx != i) continue;
@@ -1032,9 +1042,12 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // Trip 0 runs the same body: its "step 1 of the previous tile" MFMAs use
   // zeroed fragments and add exactly 0.
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) fa[1][fm] = zero_h8();
+  for (int u = 0; u < SPH; ++u) {
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
+    for (int fm = 0; fm < FM; ++fm) fa[1][u][fm] = zero_h8();
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) fb[1][u][fn] = zero_h8();
+  }
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt is in A stage kt % SA and B stage kt % 2; this trip copies B of
     // tile kt+1 and A of tile kt+SA-1 into the stages tile kt-1 left
@@ -1050,11 +1063,15 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   }
   // the last tile's step 1 (its fragments were read in the last trip)
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int u = 0; u < SPH; ++u)
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][u][fn], fa[1][u][fm], acc[fm][fn]);
   if constexpr (SA == 3) wait_all();  // A copies past the last tile drain before exit
 
+  // lane l holds, per MFMA block, output row l % MF and columns
+  // g * (256 / MF) + 4 * (l / MF) + e for g < NACC / 4, e < 4
   char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
   if ((N & 3) == 0) {
@@ -1062,22 +1079,30 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     for (int fm = 0; fm < FM; ++fm) {
       const int i = wm * WTM + fm * MF + lane % MF;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
-        Op::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, acc[fm][fn]);
-      }
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          typename Op::acc4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * g + e];
+          Op::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, v);
+        }
     }
   } else {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int i = wm * WTM + fm * MF + lane % MF;
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int j = n0 + wn * WTN + fn * MF + 4 * (lane / MF);
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB, acc[fm][fn][e]);
-      }
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB,
+                       acc[fm][fn][4 * g + e]);
+        }
     }
   }
 }
@@ -1091,9 +1116,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile_kernel(GemmArgs p) {
   d2tile_body<OpI8, BM, BN, WGM, WGN, 2>(p);
 }
 // Three A stages: A's copies are issued two trips ahead, B's one.
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int MF>
 __global__ void __launch_bounds__(64 * WGM * WGN) d2tile3_kernel(GemmArgs p) {
-  d2tile_body<OpF16, BM, BN, WGM, WGN, 3>(p);
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 3, MF>(p);
 }
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile3_kernel(GemmArgs p) {
@@ -1878,10 +1903,10 @@ hipError_t launch_generic(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int MF>
 hipError_t launch_d2tile3(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((d2tile3_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g), dim3(64 * WGM * WGN),
+  hipLaunchKernelGGL((d2tile3_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g), dim3(64 * WGM * WGN),
                      0, s, a);
   return hipGetLastError();
 }

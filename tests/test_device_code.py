@@ -29,10 +29,10 @@ def mangled(name):
     if m:
         bm, bn, wm, wn = m.groups()
         return f"_ZN4mihg13d2tile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
-    m = re.fullmatch(r"(d2tile3s?)_(\d+)x(\d+)_w(\d+)x(\d+)_m16", name)
+    m = re.fullmatch(r"d2tile3_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
     if m:
-        kind, bm, bn, wm, wn = m.groups()
-        return f"_ZN4mihg{len(kind) + 7}{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
+        bm, bn, wm, wn, mf = m.groups()
+        return f"_ZN4mihg14d2tile3_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"pptile_(\d+)x(\d+)_w8_m16", name)
     if m:
         bm, bn = m.groups()
@@ -66,7 +66,7 @@ def mangled_i8(name):
     if m:
         bm, bn, wm, wn = m.groups()
         return f"_ZN4mihg16i8_d2tile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
-    m = re.fullmatch(r"(d2tile3s?)_(\d+)x(\d+)_w(\d+)x(\d+)_m16", name)
+    m = re.fullmatch(r"(d2tile3)_(\d+)x(\d+)_w(\d+)x(\d+)_m16", name)
     if m:
         kind, bm, bn, wm, wn = m.groups()
         return (f"_ZN4mihg{len(kind) + 10}i8_{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}"
