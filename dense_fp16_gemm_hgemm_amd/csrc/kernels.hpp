@@ -1342,7 +1342,7 @@ pptile_kernel(GemmArgs p) {
 // 256- and 512-byte rows.  A copy instruction fills a 1 KiB block of
 // RPB = 8/KB rows; lane l lands on row l / (8*KB) of the block, physical
 // chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
-template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S>
+template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S>
 __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<16>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -1363,11 +1363,19 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
   static_assert(BM % (RPB * NW) == 0 && BN % (RPB * NW) == 0, "copy blocks must split evenly");
   static_assert(BM % 16 == 0, "B's rows start at a multiple of 16 LDS rows");
-  static_assert(S * STAGE * 2 <= 160 * 1024, "LDS budget");
+  // LDS: S stages of A and SB of B.  SB = S: stage s holds A then B rows at
+  // s * STAGE.  SB = S - 1: the A ring, then the B ring; A is copied one
+  // trip further ahead than B (B's copies go first, see the trip-end wait).
+  static_assert(SB == S || SB == S - 1, "B has as many stages as A, or one fewer");
+  static_assert(SB >= 2, "at least two B stages");
+  constexpr int A_STRIDE = SB == S ? STAGE : BM * ROWH;
+  constexpr int B_OFF = SB == S ? BM * ROWH : S * BM * ROWH;
+  constexpr int B_STRIDE = SB == S ? STAGE : BN * ROWH;
+  constexpr int LDS_HALVES = SB == S ? S * STAGE : S * BM * ROWH + SB * BN * ROWH;
+  static_assert(LDS_HALVES * 2 <= 160 * 1024, "LDS budget");
   static_assert(ND * (S - 2) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) _Float16 lds[S * STAGE];
-  __shared__ int s_last;
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[LDS_HALVES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -1404,16 +1412,27 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   const bool mask_k = ((k_end - k_begin) % BK) != 0;
   const uint32_t lds0 = lds_addr(lds);
   // k0: the trip's first k (absolute); chunks at or past the slice's end read 0
-  auto dma_one = [&](int st, int k0, int x) {
-    const uint32_t sbase = lds0 + (uint32_t)(st * STAGE * 2);
-    const bool kin = !mask_k || (k0 + c_k[x] < k_end);
-    if (x < A_BLK) {
-      const int blk = wave_u * A_BLK + x;
-      dma16(rda, kin ? c_off[x] : kOOB, (uint32_t)k0 * EB, sbase + (uint32_t)(blk * 1024));
+  // copy xa of A (tile at k0) into A stage ast, copy xb of B into B stage bst
+  auto dma_a = [&](int ast, int k0, int xa) {
+    const bool kin = !mask_k || (k0 + c_k[xa] < k_end);
+    const int blk = wave_u * A_BLK + xa;
+    dma16(rda, kin ? c_off[xa] : kOOB, (uint32_t)k0 * EB,
+          lds0 + (uint32_t)(ast * A_STRIDE * 2 + blk * 1024));
+  };
+  auto dma_b = [&](int bst, int k0, int xb) {
+    const bool kin = !mask_k || (k0 + c_k[A_BLK + xb] < k_end);
+    const int blk = wave_u * B_BLK + xb;
+    dma16(rdb, kin ? c_off[A_BLK + xb] : kOOB, (uint32_t)k0 * EB,
+          lds0 + (uint32_t)((B_OFF + bst * B_STRIDE) * 2 + blk * 1024));
+  };
+  // copy x of a trip: A's then B's (SB = S), or B's then A's (SB = S - 1)
+  auto dma_one = [&](int ast, int bst, int ka, int kb, int x) {
+    if constexpr (SB == S) {
+      if (x < A_BLK) dma_a(ast, ka, x);
+      else dma_b(bst, kb, x - A_BLK);
     } else {
-      const int blk = wave_u * B_BLK + (x - A_BLK);
-      dma16(rdb, kin ? c_off[x] : kOOB, (uint32_t)k0 * EB,
-            sbase + (uint32_t)(BM * ROWH * 2 + blk * 1024));
+      if (x < B_BLK) dma_b(bst, kb, x);
+      else dma_a(ast, ka, x - B_BLK);
     }
   };
 
@@ -1428,12 +1447,12 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
     fb_off[s] = (BM + wn * WTN + frow) * ROWH + phys * 8;
   }
   h8 fa[2][FM], fb[2][FN];  // [step & 1]
-  auto fread_one = [&](int st, int s, int r) {
-    const _Float16* base = lds + st * STAGE;
+  auto fread_one = [&](int ast, int bst, int s, int r) {
     if (r < FM)
-      fa[s & 1][r] = *reinterpret_cast<const h8*>(base + fa_off[s] + r * MF * ROWH);
+      fa[s & 1][r] = *reinterpret_cast<const h8*>(lds + ast * A_STRIDE + fa_off[s] + r * MF * ROWH);
     else
-      fb[s & 1][r - FM] = *reinterpret_cast<const h8*>(base + fb_off[s] + (r - FM) * MF * ROWH);
+      fb[s & 1][r - FM] = *reinterpret_cast<const h8*>(lds + B_OFF - BM * ROWH + bst * B_STRIDE +
+                                                       fb_off[s] + (r - FM) * MF * ROWH);
   };
 
   typename MM::acc_t acc[FM][FN];
@@ -1449,7 +1468,7 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   // fragment reads of step J -- and, in part 0, the copies of the tile S - 1
   // ahead -- spread evenly over the MFMA slots (copies and reads alternate
   // while copies last).
-  auto part = [&](auto JC, int rst, int kcopy, int wst) {
+  auto part = [&](auto JC, int rast, int rbst, int ka, int kb, int wast, int wbst) {
     constexpr int J = decltype(JC)::value;
     constexpr int sm = (J + KSTEPS - 1) % KSTEPS;
     constexpr int nd = J == 0 ? ND : 0;
@@ -1463,12 +1482,12 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
       for (int x = 0; x < nx; ++x) {
         if (x * NM / nx != i) continue;
         if (x < 2 * npair) {
-          if (x % 2 == 0) dma_one(wst, kcopy, x / 2);
-          else fread_one(rst, J, x / 2);
+          if (x % 2 == 0) dma_one(wast, wbst, ka, kb, x / 2);
+          else fread_one(rast, rbst, J, x / 2);
         } else if (nd > NR) {
-          dma_one(wst, kcopy, x - npair);
+          dma_one(wast, wbst, ka, kb, x - npair);
         } else {
-          fread_one(rst, J, x - npair);
+          fread_one(rast, rbst, J, x - npair);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1479,15 +1498,21 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
     constexpr int n = decltype(NC)::value;
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   };
-  using WaitInFlight = std::integral_constant<int, ND * (S - 2)>;
+  // at a trip's end the copies issued after the next tile's may stay in flight
+  using WaitInFlight = std::integral_constant<int, A_BLK * (S - 2) + B_BLK * (SB - 2)>;
   using WaitAll = std::integral_constant<int, 0>;
 
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  // prologue: tiles 0 .. S-2 into stages 0 .. S-2, tile 0 published
+  // prologue: A tiles 0 .. S-2 and B tiles 0 .. SB-2 into their stages, tile 0 published
 #pragma unroll
-  for (int t0 = 0; t0 < S - 1; ++t0)
+  for (int t0 = 0; t0 < S - 1; ++t0) {
 #pragma unroll
-    for (int x = 0; x < ND; ++x) dma_one(t0, k_begin + t0 * BK, x);
+    for (int x = 0; x < A_BLK; ++x) dma_a(t0, k_begin + t0 * BK, x);
+    if (t0 < SB - 1) {
+#pragma unroll
+      for (int x = 0; x < B_BLK; ++x) dma_b(t0, k_begin + t0 * BK, x);
+    }
+  }
   wait_vm(WaitInFlight{});
   __syncthreads();
   // trip 0's part 0 runs "the last step of tile -1" on zeroed fragments (adds 0)
@@ -1496,17 +1521,18 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt % S, wst = (kt + S - 1) % S;
-    const int kcopy = k_begin + (kt + S - 1) * BK;
-    part(std::integral_constant<int, 0>{}, st, kcopy, wst);
-    part(std::integral_constant<int, 1>{}, st, 0, 0);
-    part(std::integral_constant<int, 2>{}, st, 0, 0);
-    part(std::integral_constant<int, 3>{}, st, 0, 0);
+    const int ast = kt % S, wast = (kt + S - 1) % S;
+    const int bst = SB == S ? ast : kt % SB, wbst = SB == S ? wast : (kt + SB - 1) % SB;
+    const int ka = k_begin + (kt + S - 1) * BK, kb = k_begin + (kt + SB - 1) * BK;
+    part(std::integral_constant<int, 0>{}, ast, bst, ka, kb, wast, wbst);
+    part(std::integral_constant<int, 1>{}, ast, bst, 0, 0, 0, 0);
+    part(std::integral_constant<int, 2>{}, ast, bst, 0, 0, 0, 0);
+    part(std::integral_constant<int, 3>{}, ast, bst, 0, 0, 0, 0);
     if constexpr (KSTEPS == 8) {
-      part(std::integral_constant<int, 4>{}, st, 0, 0);
-      part(std::integral_constant<int, 5>{}, st, 0, 0);
-      part(std::integral_constant<int, 6>{}, st, 0, 0);
-      part(std::integral_constant<int, 7>{}, st, 0, 0);
+      part(std::integral_constant<int, 4>{}, ast, bst, 0, 0, 0, 0);
+      part(std::integral_constant<int, 5>{}, ast, bst, 0, 0, 0, 0);
+      part(std::integral_constant<int, 6>{}, ast, bst, 0, 0, 0, 0);
+      part(std::integral_constant<int, 7>{}, ast, bst, 0, 0, 0, 0);
     }
     wait_vm(WaitInFlight{});  // tile kt+1 has landed (later tiles may still be in flight)
     __syncthreads();
@@ -1518,7 +1544,10 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][fn], fa[1][fm], acc[fm][fn]);
   wait_vm(WaitAll{});  // copies of tiles past the end are drained before the workgroup exits
   if (splitk > 1) {
-    if (!splitk_fixup<FM, FN, NT>(acc, p, tile_id, slice, splitk, tid, &s_last)) return;
+    // the fix-up's flag word reuses the first LDS word: the fix-up's first
+    // barrier comes after every wave's last fragment read and drained copy
+    if (!splitk_fixup<FM, FN, NT>(acc, p, tile_id, slice, splitk, tid, reinterpret_cast<int*>(lds)))
+      return;
   }
 
   char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
@@ -1548,13 +1577,13 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int KB, int S>
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 __global__ void __launch_bounds__(64 * WGM * WGN) ktile_kernel(GemmArgs p) {
-  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S>(p);
+  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S, SB>(p);
 }
-template <int BM, int BN, int WGM, int WGN, int KB, int S>
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_kernel(GemmArgs p) {
-  ktile_body<OpI8, BM, BN, WGM, WGN, KB, S>(p);
+  ktile_body<OpI8, BM, BN, WGM, WGN, KB, S, SB>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1879,10 +1908,10 @@ hipError_t launch_pptile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int KB, int S>
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 hipError_t launch_ktile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
-  hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
+  hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
@@ -1919,10 +1948,10 @@ hipError_t launch_i8_d2tile3(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int KB, int S>
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 hipError_t launch_i8_ktile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
-  hipLaunchKernelGGL((i8_ktile_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
+  hipLaunchKernelGGL((i8_ktile_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }

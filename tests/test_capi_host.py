@@ -151,8 +151,8 @@ def test_heuristic_picks_by_shape(inspect_handle):
     assert choice(8192, 8192, 8192) == ("d2tile_256x256_w2x4_m16", 1)
     assert choice(1024, 14336, 4096) == ("d2tile_256x256_w2x4_m16", 1)
     # then deep-K 128x128 tiles while there are 128 of them
-    assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x2_k128_s2", 1)
-    assert choice(256, 11008, 4096) == ("ktile_128x128_w2x2_k128_s2", 1)
+    assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
+    assert choice(256, 11008, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
     # then 64x64, split over K when the tiles are few and K is long
     assert choice(256, 4096, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
     assert choice(64, 11008, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
@@ -311,7 +311,7 @@ def test_int8_alignment_class_and_heuristic(inspect_handle):
         n, _ = choice(M, N, K)
         assert n.startswith("i8_") and n != names[generic], (M, N, K, n)
     assert choice(8192, 8192, 8192)[0] == "i8_d2tile3_256x256_w2x4_m16"
-    assert choice(1024, 4096, 4096)[0] == "i8_ktile_128x128_w2x2_k256_s2"
+    assert choice(1024, 4096, 4096)[0] == "i8_ktile_128x128_w2x4_k256_s3b2"
     assert choice(16, 4096, 4096)[0] == "i8_ktile_16x64_w1x4_k256_s3"
     # the 16-byte class in int8 elements: K, lda, ldb multiples of 16, ldc of 4
     assert plan_i8(h, 256, 256, 264)[1] == generic              # K = 8 mod 16

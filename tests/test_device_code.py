@@ -42,11 +42,11 @@ def mangled(name):
         kind, bm, bn, wm, wn, mf, x = m.groups()
         return (f"_ZN4mihg12{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}ELi{x}"
                 "EEEvNS_8GemmArgsE")
-    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)", name)
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)(?:b(\d+))?", name)
     if m:
-        bm, bn, wm, wn, bk, s = m.groups()
+        bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg12ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
-                "EEEvNS_8GemmArgsE")
+                f"ELi{sb or s}EEEvNS_8GemmArgsE")
     m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)(?:_d(\d+))?", name)
     if m:
         fm, fn, w, u, d = m.groups()
@@ -71,11 +71,11 @@ def mangled_i8(name):
         kind, bm, bn, wm, wn = m.groups()
         return (f"_ZN4mihg{len(kind) + 10}i8_{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}"
                 "EEEvNS_8GemmArgsE")
-    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)", name)
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)(?:b(\d+))?", name)
     if m:
-        bm, bn, wm, wn, bk, s = m.groups()
+        bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg15i8_ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 128}"
-                f"ELi{s}EEEvNS_8GemmArgsE")
+                f"ELi{s}ELi{sb or s}EEEvNS_8GemmArgsE")
     raise AssertionError(f"unrecognised int8 kernel name {name}")
 
 
