@@ -209,7 +209,7 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   };
   // the int8 instances with the same tiles and a K step of the same bytes
   const bool i8 = dtype == mihg::DTYPE_I8;
-  const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile_256x256_w2x4_m16");
+  const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16");
   const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2");
   const int k64 = find_kernel(i8 ? "i8_ktile_64x64_w2x2_k256_s3" : "ktile_64x64_w2x2_k128_s3");
   const int k32 = find_kernel(i8 ? "i8_ktile_32x64_w2x2_k256_s3" : "ktile_32x64_w2x2_k128_s3");
