@@ -54,6 +54,7 @@ namespace mihg {
 // D2TILE3: X(BM, BN, WGM, WGN, MF): d2tile with three A stages (A copied two
 // trips ahead), MFMA 16x16x32 or 32x32x16
 #define MIHG_D2TILE3_INSTANCES(X) \
+  X(256, 192, 2, 2, 16)           \
   X(256, 256, 2, 4, 16)           \
   X(256, 256, 2, 2, 16)           \
   X(256, 256, 2, 4, 32)           \
