@@ -379,3 +379,29 @@ def test_run_kernel_rejects_operands_of_the_other_type():
             h.run_kernel("ktile_64x64_w2x2_k128_s3", b, b)
     finally:
         h.close()
+
+
+def test_shipped_table_loads_whole_and_dispatches_its_entries(monkeypatch):
+    """Every line of the shipped table names a compiled instance of the right
+    class with a valid raster, and is what dispatch picks for its shape."""
+    monkeypatch.delenv("MI_HGEMM_TABLE", raising=False)
+    path = os.path.join(os.path.dirname(mh.LIB_PATH), "tables", "gfx950.tsv")
+    rows = [ln.split() for ln in open(path, encoding="utf-8")
+            if ln.strip() and not ln.lstrip().startswith("#")]
+    st, h = mh.mi_hgemm_create_ex(path, mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK
+    try:
+        assert mh.mi_hgemm_table_size(h) == len(rows)
+        names = mh.kernel_names()
+        for r in rows:
+            M, N, K = int(r[1]), int(r[2]), int(r[3])
+            kernel, gm, xcd = r[6], int(r[7]), int(r[8])
+            split = int(r[10]) if len(r) > 10 else 1
+            assert r[0] == "gfx950" and r[4] == "TN"
+            fn = plan_i8 if r[5].startswith("i8") else plan
+            got = fn(h, M, N, K)
+            assert got[0] == mh.MI_HGEMM_OK, r
+            assert (names[got[1]], got[2], got[3]) == (kernel, gm, xcd), r
+            assert got[4] <= split, r
+    finally:
+        mh.mi_hgemm_destroy(h)
