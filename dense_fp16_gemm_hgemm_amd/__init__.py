@@ -253,6 +253,8 @@ class Hgemm:
         elif tuple(out.shape) != (M, N):
             raise ValueError(f"out must have shape {(M, N)}")
         ldc = _operand(out, "out", out_t)
+        if out.device != A.device:
+            raise ValueError("out must be on the operands' device")
         return M, N, K, lda, ldb, ldc, out
 
     def run(self, A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None,

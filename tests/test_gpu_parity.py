@@ -270,6 +270,13 @@ def test_invalid_arguments_raise(lib):
     with pytest.raises(mh.HgemmError) as ei:
         lib.tune(64, 64, 60)                   # K % 8 != 0: nothing to tune
     assert ei.value.status == mh.MI_HGEMM_ERR_UNSUPPORTED
+    # the binding checks tensors before anything reaches the C ABI
+    with pytest.raises(ValueError):
+        lib.run(A, Bt, out=torch.empty((4, 4), dtype=torch.float16))       # out on the host
+    with pytest.raises(ValueError):
+        lib.run(A, Bt[:, :4].contiguous())                                # K mismatch
+    with pytest.raises(TypeError):
+        lib.run(A, Bt, out=torch.empty((4, 4), dtype=torch.float32, device=DEV))
 
 
 def test_tuner_builds_a_table_entry(tmp_path):
