@@ -11,7 +11,7 @@ Two layers:
   * ``Hgemm``, a handle wrapper taking torch tensors and raising ``HgemmError``.
 
 Importing fails loudly when the library has not been built
-(``python -m dense_fp16_gemm_hgemm_amd.build``); there is no fallback path.
+(``python dense_fp16_gemm_hgemm_amd/build.py``); there is no fallback path.
 """
 from __future__ import annotations
 
@@ -49,7 +49,7 @@ MI_HGEMM_TUNE_INT8 = 8
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_hgemm.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m dense_fp16_gemm_hgemm_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built: run `python dense_fp16_gemm_hgemm_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 
 _i64, _i32, _u32, _p = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p

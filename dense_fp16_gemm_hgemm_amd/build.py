@@ -11,7 +11,7 @@ overlap micro-benchmark, ``overlap/overlap.hip``) and
 load generator (``serve/serve_bench.cpp``), linked against the library (found
 beside it at run time) and rocBLAS (the vendor backend it compares with).
 
-Usage: ``python -m dense_fp16_gemm_hgemm_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python dense_fp16_gemm_hgemm_amd/build.py`` (or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
 

@@ -27,7 +27,7 @@ import torch  # imported first so that both use one HIP runtime
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi_overlap.so")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m dense_fp16_gemm_hgemm_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built: run `python dense_fp16_gemm_hgemm_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 _lib.mi_overlap_run.restype = ctypes.c_int
 _lib.mi_overlap_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,

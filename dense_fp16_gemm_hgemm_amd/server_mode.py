@@ -29,7 +29,7 @@ def run(mnk: str = "64_4096_64", mode: str = "poisson", qps: float = 100.0,
         backend: str = "mi_hgemm", dump: str | None = None, timeout: float = 300.0) -> dict:
     """Run one server-mode measurement; returns the load generator's record."""
     if not os.path.exists(BINARY):
-        raise FileNotFoundError(f"{BINARY} is not built: run `python -m dense_fp16_gemm_hgemm_amd.build`")
+        raise FileNotFoundError(f"{BINARY} is not built: run `python dense_fp16_gemm_hgemm_amd/build.py`")
     cmd = [BINARY, "--mnk", mnk, "--mode", mode, "--qps", repr(float(qps)),
            "--requests", str(requests), "--depth", str(depth), "--sets", str(sets),
            "--seed", str(seed), "--backend", backend]
