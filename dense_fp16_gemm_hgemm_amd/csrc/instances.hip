@@ -86,6 +86,24 @@ namespace mihg {
   X(16, 64, 1, 4, 256, 3)          \
   X(16, 64, 1, 4, 512, 3)
 
+// KTILE_NT: X(BM, BN, WGM, WGN, BK, S) as KTILE, B copied non-temporally; the
+// tiles that serve outputs of at most 64 rows, where B is streamed once
+#define MIHG_KTILE_NT_INSTANCES(X) \
+  X(64, 64, 2, 2, 128, 3)          \
+  X(64, 128, 2, 2, 128, 3)         \
+  X(32, 64, 2, 2, 128, 3)          \
+  X(16, 64, 1, 4, 256, 3)          \
+  X(16, 64, 1, 4, 128, 3)          \
+  X(16, 128, 1, 4, 128, 3)         \
+  X(16, 16, 1, 1, 256, 3)          \
+  X(16, 32, 1, 2, 256, 3)
+
+#define MIHG_I8_KTILE_NT_INSTANCES(X) \
+  X(64, 64, 2, 2, 256, 3)             \
+  X(32, 64, 2, 2, 256, 3)             \
+  X(16, 64, 1, 4, 256, 3)             \
+  X(16, 64, 1, 4, 512, 3)
+
 // KTILE_B: X(BM, BN, WGM, WGN, BK, S, SB): S stages of A, SB = S - 1 of B
 #define MIHG_KTILE_B_INSTANCES(X) \
   X(128, 128, 2, 2, 128, 3, 2)     \
@@ -143,6 +161,10 @@ namespace mihg {
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S, S>(GemmArgs);
 #define INSTANTIATE_KTILE_B(BM, BN, WGM, WGN, BK, S, SB) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S, SB>(GemmArgs);
+#define INSTANTIATE_KTILE_NT(BM, BN, WGM, WGN, BK, S) \
+  template __global__ void ktile_nt_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
+#define INSTANTIATE_I8_KTILE_NT(BM, BN, WGM, WGN, BK, S) \
+  template __global__ void i8_ktile_nt_kernel<BM, BN, WGM, WGN, BK / 128, S>(GemmArgs);
 #define INSTANTIATE_I8_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void i8_d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_I8_KTILE(BM, BN, WGM, WGN, BK, S) \
@@ -159,12 +181,14 @@ MIHG_D2TILE3_INSTANCES(INSTANTIATE_D2TILE3)
 MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
+MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
 MIHG_I8_D2TILE_INSTANCES(INSTANTIATE_I8_D2TILE)
 MIHG_I8_D2TILE3_INSTANCES(INSTANTIATE_I8_D2TILE3)
 MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 MIHG_I8_KTILE_B_INSTANCES(INSTANTIATE_I8_KTILE_B)
+MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
 
 // The registry holds host launch functions, so it exists only in the host pass.
 #if !defined(__HIP_DEVICE_COMPILE__)
@@ -198,6 +222,14 @@ MIHG_I8_KTILE_B_INSTANCES(INSTANTIATE_I8_KTILE_B)
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "b" #SB, FAMILY_TILE, BM, BN, BK,   \
    WGM * WGN, 16, 1, 1, (S * BM + SB * BN) * BK * 2, 1,                                        \
    &launch_ktile<BM, BN, WGM, WGN, BK / 64, S, SB>, &grid_tile<BM, BN>},
+#define KTILE_NT_DESC(BM, BN, WGM, WGN, BK, S)                                              \
+  {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "_nt", FAMILY_TILE, BM, BN, BK,     \
+   WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1,                                             \
+   &launch_ktile_nt<BM, BN, WGM, WGN, BK / 64, S>, &grid_tile<BM, BN>},
+#define I8_KTILE_NT_DESC(BM, BN, WGM, WGN, BK, S)                                           \
+  {"i8_ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "_nt", FAMILY_TILE, BM, BN, BK, \
+   WGM * WGN, 16, 1, 1, S * (BM + BN) * BK, 1,                                                 \
+   &launch_i8_ktile_nt<BM, BN, WGM, WGN, BK / 128, S>, &grid_tile<BM, BN>, DTYPE_I8},
 #define I8_D2TILE_DESC(BM, BN, WGM, WGN)                                                    \
   {"i8_d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN, 16, \
    1, 1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_i8_d2tile<BM, BN, WGM, WGN>,                   \
@@ -225,6 +257,7 @@ const KernelDesc kKernels[] = {
     MIHG_PPTILE_INSTANCES(PPTILE_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_KTILE_B_INSTANCES(KTILE_B_DESC)
+    MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
     // int8 variant: element-wise instance first, then the vector-load tiles
     {"i8_generic_64x64_w2x2_m16", FAMILY_TILE, 64, 64, 128, 4, 16, 0, 1, 128 * 64 * 2, 0,
@@ -233,6 +266,7 @@ const KernelDesc kKernels[] = {
     MIHG_I8_D2TILE3_INSTANCES(I8_D2TILE3_DESC)
     MIHG_I8_KTILE_INSTANCES(I8_KTILE_DESC)
     MIHG_I8_KTILE_B_INSTANCES(I8_KTILE_B_DESC)
+    MIHG_I8_KTILE_NT_INSTANCES(I8_KTILE_NT_DESC)
 };
 
 const int kNumKernels = (int)(sizeof(kKernels) / sizeof(kKernels[0]));

@@ -463,6 +463,18 @@ __device__ inline void dma16(const u32x4& rsrc, uint32_t voff, uint32_t soff, ui
                : "memory", "m0");
 }
 
+// dma16 with the non-temporal cache policy: the lines are fetched for this
+// copy and not kept for reuse.  For an operand that is streamed through once
+// (B when the output has few tile rows) it leaves the L2 and MALL to the
+// operand that is reused (A, read by every column of tiles).
+__device__ inline void dma16_nt(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
 template <int BM, int BN>
 struct DStages {
   static constexpr int kStage = (BM + BN) * kDRow;
@@ -1342,7 +1354,7 @@ pptile_kernel(GemmArgs p) {
 // 256- and 512-byte rows.  A copy instruction fills a 1 KiB block of
 // RPB = 8/KB rows; lane l lands on row l / (8*KB) of the block, physical
 // chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
-template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S>
+template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S, bool B_NT = false>
 __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<16>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -1422,8 +1434,10 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   auto dma_b = [&](int bst, int k0, int xb) {
     const bool kin = !mask_k || (k0 + c_k[A_BLK + xb] < k_end);
     const int blk = wave_u * B_BLK + xb;
-    dma16(rdb, kin ? c_off[A_BLK + xb] : kOOB, (uint32_t)k0 * EB,
-          lds0 + (uint32_t)((B_OFF + bst * B_STRIDE) * 2 + blk * 1024));
+    const uint32_t boff = kin ? c_off[A_BLK + xb] : kOOB;
+    const uint32_t blds = lds0 + (uint32_t)((B_OFF + bst * B_STRIDE) * 2 + blk * 1024);
+    if constexpr (B_NT) dma16_nt(rdb, boff, (uint32_t)k0 * EB, blds);
+    else dma16(rdb, boff, (uint32_t)k0 * EB, blds);
   };
   // copy x of a trip: A's then B's (SB = S), or B's then A's (SB = S - 1)
   auto dma_one = [&](int ast, int bst, int ka, int kb, int x) {
@@ -1584,6 +1598,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) ktile_kernel(GemmArgs p) {
 template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_kernel(GemmArgs p) {
   ktile_body<OpI8, BM, BN, WGM, WGN, KB, S, SB>(p);
+}
+// B copied with the non-temporal policy (a tuner candidate for few tile rows)
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN) ktile_nt_kernel(GemmArgs p) {
+  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S, S, true>(p);
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+__global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_nt_kernel(GemmArgs p) {
+  ktile_body<OpI8, BM, BN, WGM, WGN, KB, S, S, true>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1912,6 +1935,20 @@ template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 hipError_t launch_ktile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
   hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+hipError_t launch_ktile_nt(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((ktile_nt_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S>
+hipError_t launch_i8_ktile_nt(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((i8_ktile_nt_kernel<BM, BN, WGM, WGN, KB, S>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }

@@ -211,9 +211,16 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   const bool i8 = dtype == mihg::DTYPE_I8;
   const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16");
   const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2");
-  const int k64 = find_kernel(i8 ? "i8_ktile_64x64_w2x2_k256_s3" : "ktile_64x64_w2x2_k128_s3");
-  const int k32 = find_kernel(i8 ? "i8_ktile_32x64_w2x2_k256_s3" : "ktile_32x64_w2x2_k128_s3");
-  const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3" : "ktile_16x64_w1x4_k128_s3");
+  // When the output is one row of tiles B is streamed through once: those
+  // tiles copy it with the non-temporal policy ("_nt"), which
+  // leaves the caches to A (measured 1-10% faster on the 16- and 64-row
+  // projection shapes).
+  const bool one_row = M <= 64;
+  const int k64 = find_kernel(i8 ? (one_row ? "i8_ktile_64x64_w2x2_k256_s3_nt" : "i8_ktile_64x64_w2x2_k256_s3")
+                                 : (one_row ? "ktile_64x64_w2x2_k128_s3_nt" : "ktile_64x64_w2x2_k128_s3"));
+  const int k32 = find_kernel(i8 ? (M <= 32 ? "i8_ktile_32x64_w2x2_k256_s3_nt" : "i8_ktile_32x64_w2x2_k256_s3")
+                                 : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3"));
+  const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3_nt" : "ktile_16x64_w1x4_k128_s3_nt");
   if (M > 64 && k256 >= 0 && tiles(k256) >= 128) {
     pick(k256, 8, 1, 1);
   } else if (M > 64 && k128 >= 0 && tiles(k128) >= 128) {
@@ -812,6 +819,9 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
       }) == cands.end())
     cands.push_back(start);
 
+  // MI_HGEMM_TUNE_LOG=1 prints every timed candidate to stderr
+  const char* log_env = std::getenv("MI_HGEMM_TUNE_LOG");
+  const bool log_search = log_env && *log_env && std::strcmp(log_env, "0") != 0;
   Config best;
   best.kernel = -1;
   double best_us = 1e300;
@@ -861,6 +871,10 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
       break;
     }
     const double us = median(trials);
+    if (log_search)
+      std::fprintf(stderr, "mi_hgemm_tune %lld %lld %lld %s g%d x%d s%d %.3f us\n", (long long)M,
+                   (long long)N, (long long)K, kKernels[cand.kernel].name, cand.group_m,
+                   cand.xcd, cand.splitk, us);
     if (us < best_us) {
       best_us = us;
       best = cand;

@@ -156,7 +156,9 @@ mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int
  * multiple of 16 and at most 131071); their check and timing operands are
  * uniform random int8 and the reference is the element-wise int8 instance.
  * Synchronises `stream`.  Allocates scratch (the operand sets and two
- * outputs, freed before returning).
+ * outputs, freed before returning).  With the environment variable
+ * MI_HGEMM_TUNE_LOG set (and not "0"), every timed candidate is printed to
+ * stderr as one line: M N K kernel g<group_m> x<xcd_remap> s<split> µs.
  * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
  */
 mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,

@@ -153,15 +153,18 @@ def test_heuristic_picks_by_shape(inspect_handle):
     # then deep-K 128x128 tiles while there are 128 of them
     assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
     assert choice(256, 11008, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
-    # then 64x64, split over K when the tiles are few and K is long
+    # then 64x64, split over K when the tiles are few and K is long; when the
+    # output is one row of tiles B is streamed once and copied non-temporally
     assert choice(256, 4096, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
-    assert choice(64, 11008, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
-    assert choice(64, 4096, 11008) == ("ktile_64x64_w2x2_k128_s3", 4)
-    # M <= 64 over a short K: 32x64 tiles, split to fill the device
+    assert choice(64, 11008, 4096) == ("ktile_64x64_w2x2_k128_s3_nt", 1)
+    assert choice(64, 4096, 11008) == ("ktile_64x64_w2x2_k128_s3_nt", 4)
+    # M <= 64 over a short K: 32x64 tiles, split to fill the device (two rows
+    # of tiles read B twice: the cached copy)
     assert choice(64, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3", 2)
+    assert choice(32, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3_nt", 4)
     # 16 rows: 16x64 deep-K tiles for wide or deep shapes, skinny otherwise
-    assert choice(16, 14336, 4096) == ("ktile_16x64_w1x4_k128_s3", 1)
-    assert choice(16, 4096, 11008) == ("ktile_16x64_w1x4_k128_s3", 4)
+    assert choice(16, 14336, 4096) == ("ktile_16x64_w1x4_k128_s3_nt", 1)
+    assert choice(16, 4096, 11008) == ("ktile_16x64_w1x4_k128_s3_nt", 4)
     assert choice(16, 4096, 4096) == ("skinny_1x1_w4_u4", 1)
     # a short K is never split
     assert choice(256, 4096, 1024)[1] == 1
@@ -312,7 +315,7 @@ def test_int8_alignment_class_and_heuristic(inspect_handle):
         assert n.startswith("i8_") and n != names[generic], (M, N, K, n)
     assert choice(8192, 8192, 8192)[0] == "i8_d2tile3_256x256_w2x4_m16"
     assert choice(1024, 4096, 4096)[0] == "i8_ktile_128x128_w2x4_k256_s3b2"
-    assert choice(16, 4096, 4096)[0] == "i8_ktile_16x64_w1x4_k256_s3"
+    assert choice(16, 4096, 4096)[0] == "i8_ktile_16x64_w1x4_k256_s3_nt"
     # the 16-byte class in int8 elements: K, lda, ldb multiples of 16, ldc of 4
     assert plan_i8(h, 256, 256, 264)[1] == generic              # K = 8 mod 16
     assert plan_i8(h, 256, 256, 256, lda=264)[1] == generic

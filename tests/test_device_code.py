@@ -47,6 +47,11 @@ def mangled(name):
         bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg12ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
                 f"ELi{sb or s}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)_nt", name)
+    if m:
+        bm, bn, wm, wn, bk, s = m.groups()
+        return (f"_ZN4mihg15ktile_nt_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
+                "EEEvNS_8GemmArgsE")
     m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)(?:_d(\d+))?", name)
     if m:
         fm, fn, w, u, d = m.groups()
@@ -76,6 +81,11 @@ def mangled_i8(name):
         bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg15i8_ktile_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 128}"
                 f"ELi{s}ELi{sb or s}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)_nt", name)
+    if m:
+        bm, bn, wm, wn, bk, s = m.groups()
+        return (f"_ZN4mihg18i8_ktile_nt_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 128}"
+                f"ELi{s}EEEvNS_8GemmArgsE")
     raise AssertionError(f"unrecognised int8 kernel name {name}")
 
 
