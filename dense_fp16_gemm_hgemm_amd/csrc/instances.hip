@@ -104,6 +104,14 @@ namespace mihg {
   X(16, 64, 1, 4, 256, 3)             \
   X(16, 64, 1, 4, 512, 3)
 
+// Unswizzled twins of the large tiles (logical chunk = physical chunk in
+// every LDS row): tuner candidates that show what the XOR layout is worth
+#define MIHG_D2TILE3_NS_INSTANCES(X) \
+  X(256, 256, 2, 2, 16)              \
+  X(256, 256, 2, 4, 16)
+#define MIHG_KTILE_NS_B_INSTANCES(X) \
+  X(128, 128, 2, 4, 128, 3, 2)
+
 // KTILE_B: X(BM, BN, WGM, WGN, BK, S, SB): S stages of A, SB = S - 1 of B
 #define MIHG_KTILE_B_INSTANCES(X) \
   X(128, 128, 2, 2, 128, 3, 2)     \
@@ -165,6 +173,10 @@ namespace mihg {
   template __global__ void ktile_nt_kernel<BM, BN, WGM, WGN, BK / 64, S>(GemmArgs);
 #define INSTANTIATE_I8_KTILE_NT(BM, BN, WGM, WGN, BK, S) \
   template __global__ void i8_ktile_nt_kernel<BM, BN, WGM, WGN, BK / 128, S>(GemmArgs);
+#define INSTANTIATE_D2TILE3_NS(BM, BN, WGM, WGN, MF) \
+  template __global__ void d2tile3_ns_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
+#define INSTANTIATE_KTILE_NS_B(BM, BN, WGM, WGN, BK, S, SB) \
+  template __global__ void ktile_ns_kernel<BM, BN, WGM, WGN, BK / 64, S, SB>(GemmArgs);
 #define INSTANTIATE_I8_D2TILE(BM, BN, WGM, WGN) \
   template __global__ void i8_d2tile_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_I8_KTILE(BM, BN, WGM, WGN, BK, S) \
@@ -182,6 +194,8 @@ MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
 MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
+MIHG_D2TILE3_NS_INSTANCES(INSTANTIATE_D2TILE3_NS)
+MIHG_KTILE_NS_B_INSTANCES(INSTANTIATE_KTILE_NS_B)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
 MIHG_I8_D2TILE_INSTANCES(INSTANTIATE_I8_D2TILE)
@@ -230,6 +244,14 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
   {"i8_ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "_nt", FAMILY_TILE, BM, BN, BK, \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK, 1,                                                 \
    &launch_i8_ktile_nt<BM, BN, WGM, WGN, BK / 128, S>, &grid_tile<BM, BN>, DTYPE_I8},
+#define D2TILE3_NS_DESC(BM, BN, WGM, WGN, MF)                                               \
+  {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF "_noxor", FAMILY_TILE, BM, BN, 64,       \
+   WGM * WGN, MF, 1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0,                                     \
+   &launch_d2tile3_ns<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
+#define KTILE_NS_B_DESC(BM, BN, WGM, WGN, BK, S, SB)                                          \
+  {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "b" #SB "_noxor", FAMILY_TILE, BM, \
+   BN, BK, WGM * WGN, 16, 1, 1, (S * BM + SB * BN) * BK * 2, 1,                                 \
+   &launch_ktile_ns<BM, BN, WGM, WGN, BK / 64, S, SB>, &grid_tile<BM, BN>},
 #define I8_D2TILE_DESC(BM, BN, WGM, WGN)                                                    \
   {"i8_d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN, 16, \
    1, 1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_i8_d2tile<BM, BN, WGM, WGN>,                   \
@@ -258,6 +280,8 @@ const KernelDesc kKernels[] = {
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_KTILE_B_INSTANCES(KTILE_B_DESC)
     MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)
+    MIHG_D2TILE3_NS_INSTANCES(D2TILE3_NS_DESC)
+    MIHG_KTILE_NS_B_INSTANCES(KTILE_NS_B_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
     // int8 variant: element-wise instance first, then the vector-load tiles
     {"i8_generic_64x64_w2x2_m16", FAMILY_TILE, 64, 64, 128, 4, 16, 0, 1, 128 * 64 * 2, 0,

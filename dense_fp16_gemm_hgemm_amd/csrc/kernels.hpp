@@ -879,7 +879,9 @@ dtile_kernel(GemmArgs p) {
 // flight (vmcnt counts this wave's copies in issue order).
 constexpr int kD2Row = 64;  // halves per LDS row
 
-template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16>
+// XS = false stores rows unswizzled (logical chunk = physical chunk): the
+// tuner's "no swizzle" candidate, kept to measure what the XOR layout buys.
+template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16, bool XS = true>
 __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<MF>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -922,7 +924,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int drow = lane >> 3;
-  const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
+  const int dch0 = XS ? (lane & 7) ^ (lane >> 4) : lane & 7, dch1 = XS ? dch0 ^ 4 : dch0;
   const u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB,
                              (uint32_t)(min(BM, M - m0) * lda * EB));
   const u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB,
@@ -963,7 +965,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // fragments of k-step t: row base + per-lane physical chunk of logical
   // chunk CPS*t + l/MF (rows are multiples of MF plus l % MF, so the swizzle
   // term is ((l % MF) >> 1) & 7; 16 lanes read 16 consecutive rows per pass)
-  const int frow = lane % MF, fq = lane / MF, fsw = (frow >> 1) & 7;
+  const int frow = lane % MF, fq = lane / MF, fsw = XS ? (frow >> 1) & 7 : 0;
   int fa_off[KSTEPS], fb_off[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
@@ -1354,7 +1356,9 @@ pptile_kernel(GemmArgs p) {
 // 256- and 512-byte rows.  A copy instruction fills a 1 KiB block of
 // RPB = 8/KB rows; lane l lands on row l / (8*KB) of the block, physical
 // chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
-template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S, bool B_NT = false>
+// XS = false: unswizzled rows, the "no swizzle" candidate (as in d2tile_body)
+template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S, bool B_NT = false,
+          bool XS = true>
 __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<16>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -1417,7 +1421,7 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
     const bool is_a = x < A_BLK;
     const int blk = is_a ? wave_u * A_BLK + x : wave_u * B_BLK + (x - A_BLK);
     const int row = blk * RPB + lane / CPR;
-    const int c = (lane % CPR) ^ (row & 15);
+    const int c = XS ? (lane % CPR) ^ (row & 15) : lane % CPR;
     c_off[x] = (uint32_t)(row * (is_a ? lda : ldb) * EB + c * 16);
     c_k[x] = c * EPC;
   }
@@ -1456,7 +1460,7 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   int fa_off[KSTEPS], fb_off[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    const int phys = (4 * s + fq) ^ frow;
+    const int phys = XS ? (4 * s + fq) ^ frow : 4 * s + fq;
     fa_off[s] = (wm * WTM + frow) * ROWH + phys * 8;
     fb_off[s] = (BM + wn * WTN + frow) * ROWH + phys * 8;
   }
@@ -1598,6 +1602,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) ktile_kernel(GemmArgs p) {
 template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_kernel(GemmArgs p) {
   ktile_body<OpI8, BM, BN, WGM, WGN, KB, S, SB>(p);
+}
+// unswizzled LDS rows (tuner candidates that measure the XOR layout's worth)
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tile3_ns_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 3, MF, false>(p);
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
+__global__ void __launch_bounds__(64 * WGM * WGN) ktile_ns_kernel(GemmArgs p) {
+  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S, SB, false, false>(p);
 }
 // B copied with the non-temporal policy (a tuner candidate for few tile rows)
 template <int BM, int BN, int WGM, int WGN, int KB, int S>
@@ -1935,6 +1948,20 @@ template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 hipError_t launch_ktile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
   hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
+hipError_t launch_ktile_ns(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((ktile_ns_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN, int WGM, int WGN, int MF>
+hipError_t launch_d2tile3_ns(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((d2tile3_ns_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }

@@ -52,6 +52,15 @@ def mangled(name):
         bm, bn, wm, wn, bk, s = m.groups()
         return (f"_ZN4mihg15ktile_nt_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
                 "EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)b(\d+)_noxor", name)
+    if m:
+        bm, bn, wm, wn, bk, s, sb = m.groups()
+        return (f"_ZN4mihg15ktile_ns_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
+                f"ELi{sb}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"d2tile3_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)_noxor", name)
+    if m:
+        bm, bn, wm, wn, mf = m.groups()
+        return f"_ZN4mihg17d2tile3_ns_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"skinny_(\d+)x(\d+)_w(\d+)_u(\d+)(?:_d(\d+))?", name)
     if m:
         fm, fn, w, u, d = m.groups()
