@@ -304,7 +304,9 @@ SPLIT_CASES = [(256, 512, 4096, 2), (256, 512, 4096, 4), (200, 300, 2560, 3), (1
 SPLIT_KERNELS = ["dtile_128x128_w2x2_m16_s4", "dtile_256x128_w2x2_m16_s4",
                  "dtile_128x256_w2x2_m16_s4", "skinny_1x4_w4_u2", "skinny_2x2_w4_u4",
                  "skinny_4x1_w8_u2", "ktile_16x64_w1x4_k256_s3", "ktile_64x64_w2x2_k128_s3",
-                 "ktile_128x128_w2x2_k128_s2", "ktile_128x128_w2x4_k128_s3b2"]
+                 "ktile_128x128_w2x2_k128_s2", "ktile_128x128_w2x4_k128_s3b2",
+                 "ktile_16x64_w1x4_k256_s3_nt", "ktile_64x64_w2x2_k128_s3_nt",
+                 "ktile_128x128_w2x4_k128_s3b2_noxor"]
 
 
 @pytest.mark.parametrize("kernel", SPLIT_KERNELS)
