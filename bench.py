@@ -24,6 +24,7 @@ sample of the same product on the host cores.
                     [--workload i8_square|i8_llm_MxNxK]
                     [--mnk M_N_K] [--warm] [--no-cpu-baseline] [--all-configs OUT.jsonl]
                     [--kernel NAME [--group-m G] [--xcd-remap X] [--split-k S]]
+                    [--sweep OUT.jsonl [--sweep-count N]]
 """
 from __future__ import annotations
 
@@ -66,6 +67,9 @@ def parse():
     ap.add_argument("--group-m", type=int, default=1, help="raster group height with --kernel")
     ap.add_argument("--xcd-remap", type=int, default=0, choices=(0, 1), help="XCD remap with --kernel")
     ap.add_argument("--split-k", type=int, default=1, help="K split with --kernel")
+    ap.add_argument("--sweep", default=None, metavar="OUT.jsonl",
+                    help="time the seeded 1000-shape sweep (device time, cold) against torch")
+    ap.add_argument("--sweep-count", type=int, default=1000, help="first N problems of the sweep")
     ap.add_argument("--server", action="store_true",
                     help="server-mode QPS of the tiny problem (64, 4096, 64) instead")
     ap.add_argument("--target-qps", type=float, default=100.0, help="arrival rate with --server")
@@ -146,15 +150,19 @@ def problem_for(name, mnk):
 class Workload:
     """Device operand sets for one problem (copies of one seeded draw)."""
 
-    def __init__(self, p, cold: bool):
+    def __init__(self, p, cold: bool, operands=None):
         import torch
         from dense_fp16_gemm_hgemm_amd import inputs
         self.p = p
-        A, Bt = inputs.make(p)
-        self.A_host, self.Bt_host = A, Bt
         dev = torch.device("cuda", 0)
-        a = torch.from_numpy(A).to(dev)
-        b = torch.from_numpy(Bt).to(dev)
+        if operands is None:
+            A, Bt = inputs.make(p)
+            self.A_host, self.Bt_host = A, Bt
+            a = torch.from_numpy(A).to(dev)
+            b = torch.from_numpy(Bt).to(dev)
+        else:                      # device operands drawn by the caller
+            self.A_host = self.Bt_host = None
+            a, b = operands
         set_bytes = p.min_bytes
         nsets = 1
         if cold:
@@ -316,9 +324,10 @@ def graph_us(fn, wl, reps):
     return us
 
 
-def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_time=False):
+def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_time=False,
+            operands=None):
     """force: None (the library's dispatch) or (kernel name, group_m, xcd_remap, split_k)."""
-    wl = Workload(p, cold)
+    wl = Workload(p, cold, operands)
     a, b, c = wl.sets[0]
     if force is None:
         kernel, gm, xcd, sk = lib.plan(a, b, c)
@@ -349,6 +358,70 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
         if tm is not None:
             rec["torch_device_us_per_call"] = round(graph_us(tm, wl, reps), 3)
     return rec, wl
+
+
+def sweep_main(args, lib):
+    """The seeded shape sweep (each of M, N, K = 2^U{6..13}, the stand-in for the
+    pages' 1000 configurations): per problem, the device time per call (graph
+    replay over cold operand copies) through the library's dispatch, its
+    roofline fraction, and torch.matmul's device time on the same operands.
+    The operands have the sweep's distribution (randn/sqrt(K) in binary16) but
+    are drawn on the device with torch's generator, seeded with the problem's
+    seed: the numpy draws of the recipe take minutes at this volume, and the
+    timing depends on the distribution, not on the particular values (the
+    sweep's parity is tested on the recipe's own draws).  Writes one JSON line
+    per problem to args.sweep and prints a summary line."""
+    import torch
+    from dense_fp16_gemm_hgemm_amd import inputs
+    dev = torch.device("cuda", 0)
+    probs = inputs.sweep()[: args.sweep_count]
+    recs = []
+    t0 = time.perf_counter()
+    with open(args.sweep, "w") as f:
+        for i, p in enumerate(probs):
+            g = torch.Generator(device=dev).manual_seed(p.seed)
+            a = (torch.randn(p.M, p.K, device=dev, generator=g) * p.a_scale).half()
+            b = (torch.randn(p.N, p.K, device=dev, generator=g) * p.b_scale).half()
+            rec, wl = measure(lib, p, 10, 3, True, with_torch=True, device_time=True,
+                              operands=(a, b))
+            rec["operands"] = "torch.randn on the device, seeded with the problem's seed"
+            f.write(json.dumps(rec) + "\n")
+            f.flush()
+            recs.append(rec)
+            del wl, a, b
+            torch.cuda.empty_cache()
+            if (i + 1) % 25 == 0 or i + 1 == len(probs):
+                print(f"# sweep {i + 1}/{len(probs)} ({time.perf_counter() - t0:.0f} s)",
+                      file=sys.stderr, flush=True)
+    fr = [r["device_roofline"]["frac"] for r in recs]
+    ok = [r["device_roofline"]["frac"] >= (0.7 if r["device_roofline"]["bound"] == "mfma" else 0.6)
+          for r in recs]
+    sp = [r["torch_device_us_per_call"] / r["device_us_per_call"] for r in recs
+          if r.get("torch_device_us_per_call")]
+    gmean = lambda v: math.exp(statistics.fmean(math.log(max(x, 1e-12)) for x in v))
+    by_bound = {}
+    for r, o in zip(recs, ok):
+        d = by_bound.setdefault(r["device_roofline"]["bound"], {"problems": 0, "meet_target": 0, "fracs": []})
+        d["problems"] += 1
+        d["meet_target"] += int(o)
+        d["fracs"].append(r["device_roofline"]["frac"])
+    for d in by_bound.values():
+        d["geomean_frac"] = round(gmean(d.pop("fracs")), 4)
+    kernels = {}
+    for r in recs:
+        kernels[r["kernel"]] = kernels.get(r["kernel"], 0) + 1
+    summary = {
+        "sweep_problems": len(recs), "cache": "cold", "timing": "device (graph replay)",
+        "meet_target": sum(ok), "meet_target_rate": round(sum(ok) / len(recs), 4),
+        "target": "roofline frac >= 0.7 (MFMA-bound) or >= 0.6 (HBM-bound)",
+        "geomean_frac": round(gmean(fr), 4), "by_bound": by_bound,
+        "geomean_speedup_vs_torch": round(gmean(sp), 4),
+        "faster_than_torch": sum(1 for x in sp if x > 1.0),
+        "speedup_vs_torch_min": round(min(sp), 3), "speedup_vs_torch_max": round(max(sp), 3),
+        "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1])),
+        "seconds": round(time.perf_counter() - t0, 1), "source_digest": source_digest(),
+    }
+    print(json.dumps(summary), flush=True)
 
 
 def server_cpu_baseline(mnk, target_s):
@@ -445,6 +518,10 @@ def main():
     import dense_fp16_gemm_hgemm_amd as mh
     lib = mh.Hgemm()
     cold = not args.warm
+    if args.sweep:
+        sweep_main(args, lib)
+        lib.close()
+        return
 
     if args.all_configs:
         from dense_fp16_gemm_hgemm_amd import inputs

@@ -179,8 +179,10 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
 // raise reuse and lower occupancy), else a K split.  The thresholds come from
 // timing every instance over the LLM projection and square shapes on MI355X:
 //  - one partial wave of 256x256 tiles beats more waves of smaller tiles down
-//    to half a wave (the chip is power-bound: idle CUs buy clock for the busy
-//    ones);
+//    to three quarters of a wave (the chip is power-bound: idle CUs buy clock
+//    for the busy ones);
+//  - below that, two or more full waves of 128x128 direct-to-LDS tiles win, at
+//    every K (14-33% ahead of a half wave of 256x256 tiles on the shape sweep);
 //  - below that, the deep-K tiles (K step 128) win: 128x128, then 64x64, then
 //    32x64 / 16x64 for the smallest M; small tiles are latency-bound per K
 //    step, so a deep step beats more parallel tiles;
@@ -221,8 +223,11 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   const int k32 = find_kernel(i8 ? (M <= 32 ? "i8_ktile_32x64_w2x2_k256_s3_nt" : "i8_ktile_32x64_w2x2_k256_s3")
                                  : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3"));
   const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3_nt" : "ktile_16x64_w1x4_k128_s3_nt");
-  if (M > 64 && k256 >= 0 && tiles(k256) >= 128) {
+  const int k128d = find_kernel(i8 ? "i8_d2tile_128x128_w2x2_m16" : "d2tile_128x128_w2x2_m16");
+  if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
     pick(k256, 8, 1, 1);
+  } else if (M > 64 && k128d >= 0 && tiles(k128d) >= 512) {
+    pick(k128d, 8, 1, 1);
   } else if (M > 64 && k128 >= 0 && tiles(k128) >= 128) {
     pick(k128, 8, 1, split_for(k128));
   } else if (M > 32 && k64 >= 0 && (tiles(k64) >= 128 || K >= 8192)) {
