@@ -109,6 +109,11 @@ namespace mihg {
 #define MIHG_D2TILE3_NS_INSTANCES(X) \
   X(256, 256, 2, 2, 16)              \
   X(256, 256, 2, 4, 16)
+// Persistent d2tile3 (one workgroup per CU walks the tiles).  Only the 8-wave
+// form: the 4-wave one already uses every register, and the tile loop's state
+// spills it.
+#define MIHG_D2TILE3P_INSTANCES(X) \
+  X(256, 256, 2, 4, 16)
 #define MIHG_KTILE_NS_B_INSTANCES(X) \
   X(128, 128, 2, 4, 128, 3, 2)
 
@@ -175,6 +180,8 @@ namespace mihg {
   template __global__ void i8_ktile_nt_kernel<BM, BN, WGM, WGN, BK / 128, S>(GemmArgs);
 #define INSTANTIATE_D2TILE3_NS(BM, BN, WGM, WGN, MF) \
   template __global__ void d2tile3_ns_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
+#define INSTANTIATE_D2TILE3P(BM, BN, WGM, WGN, MF) \
+  template __global__ void d2tile3p_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
 #define INSTANTIATE_KTILE_NS_B(BM, BN, WGM, WGN, BK, S, SB) \
   template __global__ void ktile_ns_kernel<BM, BN, WGM, WGN, BK / 64, S, SB>(GemmArgs);
 #define INSTANTIATE_I8_D2TILE(BM, BN, WGM, WGN) \
@@ -195,6 +202,7 @@ MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
 MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
 MIHG_D2TILE3_NS_INSTANCES(INSTANTIATE_D2TILE3_NS)
+MIHG_D2TILE3P_INSTANCES(INSTANTIATE_D2TILE3P)
 MIHG_KTILE_NS_B_INSTANCES(INSTANTIATE_KTILE_NS_B)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
@@ -248,6 +256,10 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
   {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF "_noxor", FAMILY_TILE, BM, BN, 64,       \
    WGM * WGN, MF, 1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0,                                     \
    &launch_d2tile3_ns<BM, BN, WGM, WGN, MF>, &grid_tile<BM, BN>},
+#define D2TILE3P_DESC(BM, BN, WGM, WGN, MF)                                                 \
+  {"d2tile3p_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, \
+   1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3p<BM, BN, WGM, WGN, MF>,             \
+   &grid_tile<BM, BN>},
 #define KTILE_NS_B_DESC(BM, BN, WGM, WGN, BK, S, SB)                                          \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "b" #SB "_noxor", FAMILY_TILE, BM, \
    BN, BK, WGM * WGN, 16, 1, 1, (S * BM + SB * BN) * BK * 2, 1,                                 \
@@ -281,6 +293,7 @@ const KernelDesc kKernels[] = {
     MIHG_KTILE_B_INSTANCES(KTILE_B_DESC)
     MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)
     MIHG_D2TILE3_NS_INSTANCES(D2TILE3_NS_DESC)
+    MIHG_D2TILE3P_INSTANCES(D2TILE3P_DESC)
     MIHG_KTILE_NS_B_INSTANCES(KTILE_NS_B_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
     // int8 variant: element-wise instance first, then the vector-load tiles

@@ -881,7 +881,14 @@ constexpr int kD2Row = 64;  // halves per LDS row
 
 // XS = false stores rows unswizzled (logical chunk = physical chunk): the
 // tuner's "no swizzle" candidate, kept to measure what the XOR layout buys.
-template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16, bool XS = true>
+__device__ inline int ntiles_of(int tiles_m, int tiles_n) { return tiles_m * tiles_n; }
+
+// PERSIST = true: one workgroup per CU walks the output tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...; after a tile's last trip the next tile's first
+// copies are issued before this tile's last MFMAs and C stores, so their
+// latency hides behind that work instead of opening every tile.
+template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16, bool XS = true,
+          bool PERSIST = false>
 __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<MF>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -915,20 +922,21 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int M = p.M, N = p.N, K = p.K;
-  int tm, tn;
-  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tile = blockIdx.x, tm, tn;
+  tile_coords(tile, tiles_m, tiles_n, p.group_m, p.xcd_remap, tm, tn);
+  int m0 = tm * BM, n0 = tn * BN;
   const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
   // copies: lane l -> row l/8 of an 8-row block, physical chunk l%8, which
   // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int drow = lane >> 3;
   const int dch0 = XS ? (lane & 7) ^ (lane >> 4) : lane & 7, dch1 = XS ? dch0 ^ 4 : dch0;
-  const u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB,
-                             (uint32_t)(min(BM, M - m0) * lda * EB));
-  const u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB,
-                             (uint32_t)(min(BN, N - n0) * ldb * EB));
+  u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB,
+                       (uint32_t)(min(BM, M - m0) * lda * EB));
+  u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB,
+                       (uint32_t)(min(BN, N - n0) * ldb * EB));
   const uint32_t a_v0 = (uint32_t)(drow * lda * EB + dch0 * 16), a_v1 = (uint32_t)(drow * lda * EB + dch1 * 16);
   const uint32_t b_v0 = (uint32_t)(drow * ldb * EB + dch0 * 16), b_v1 = (uint32_t)(drow * ldb * EB + dch1 * 16);
   const bool mask_k = (K % BK) != 0;
@@ -1041,18 +1049,37 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
 
   const int nk = (K + BK - 1) / BK;
   // prologue: tile 0 in stage 0 (and, with SA = 3, A of tile 1 in A stage 1)
+  auto prologue_copies = [&]() {
 #pragma unroll
-  for (int x = 0; x < A_BLK; ++x) dma_a(0, 0, x);
+    for (int x = 0; x < A_BLK; ++x) dma_a(0, 0, x);
 #pragma unroll
-  for (int x = 0; x < B_BLK; ++x) dma_b(0, 0, x);
-  if constexpr (SA == 3) {
+    for (int x = 0; x < B_BLK; ++x) dma_b(0, 0, x);
+    if constexpr (SA == 3) {
 #pragma unroll
-    for (int x = 0; x < A_BLK; ++x) dma_a(1, BK, x);
-    wait_but_a();
+      for (int x = 0; x < A_BLK; ++x) dma_a(1, BK, x);
+    }
+  };
+  prologue_copies();
+  for (bool first = true;; first = false) {
+  // Persistent form: the copies' per-block addresses are recomputed for each
+  // tile instead of being hoisted out of the tile loop and held (spilled)
+  // across it; an empty asm makes the wave index opaque to that hoisting.
+  if constexpr (PERSIST) asm volatile("" : "+s"(wave_u));
+  if (first) {
+    if constexpr (SA == 3) wait_but_a();
+    else wait_all();
   } else {
-    wait_all();
+    wait_all();  // the previous tile's C stores count in vmcnt too
   }
   __syncthreads();
+  if (!first) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0;
+  }
   // Trip 0 runs the same body: its "step 1 of the previous tile" MFMAs use
   // zeroed fragments and add exactly 0.
 #pragma unroll
@@ -1075,6 +1102,24 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     else wait_all();
     __syncthreads();
   }
+  // this output tile's origin (m0, n0 move on to the next tile below)
+  const int em0 = m0, en0 = n0;
+  bool more = false;
+  if constexpr (PERSIST) {
+    if (tile + (int)gridDim.x < ntiles_of(tiles_m, tiles_n)) {
+      more = true;
+      // every fragment read of this tile finished before the last barrier;
+      // this wave's copies past the last K tile land before it refills its rows
+      wait_all();
+      tile += gridDim.x;
+      tile_coords(tile, tiles_m, tiles_n, p.group_m, p.xcd_remap, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      rda = raw_rsrc(static_cast<const char*>(p.A) + m0 * lda * EB, (uint32_t)(min(BM, M - m0) * lda * EB));
+      rdb = raw_rsrc(static_cast<const char*>(p.B) + n0 * ldb * EB, (uint32_t)(min(BN, N - n0) * ldb * EB));
+      prologue_copies();
+    }
+  }
   // the last tile's step 1 (its fragments were read in the last trip)
 #pragma unroll
   for (int u = 0; u < SPH; ++u)
@@ -1082,12 +1127,14 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][u][fn], fa[1][u][fm], acc[fm][fn]);
-  if constexpr (SA == 3) wait_all();  // A copies past the last tile drain before exit
+  if constexpr (SA == 3) {
+    if (!more) wait_all();  // A copies past the last tile drain before exit
+  }
 
   // lane l holds, per MFMA block, output row l % MF and columns
   // g * (256 / MF) + 4 * (l / MF) + e for g < NACC / 4, e < 4
-  char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
-  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
+  char* Cw = static_cast<char*>(p.C) + em0 * ldc * CB;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - em0) * ldc * CB));
   if ((N & 3) == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -1096,7 +1143,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int g = 0; g < MM::NACC / 4; ++g) {
-          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          const int j = en0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
           typename Op::acc4_t v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * g + e];
@@ -1111,7 +1158,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int g = 0; g < MM::NACC / 4; ++g) {
-          const int j = n0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          const int j = en0 + wn * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB,
@@ -1119,8 +1166,9 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
         }
     }
   }
+  if (!more) break;
+  }
 }
-
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN) d2tile_kernel(GemmArgs p) {
   d2tile_body<OpF16, BM, BN, WGM, WGN, 2>(p);
@@ -1137,6 +1185,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) d2tile3_kernel(GemmArgs p) {
 template <int BM, int BN, int WGM, int WGN>
 __global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile3_kernel(GemmArgs p) {
   d2tile_body<OpI8, BM, BN, WGM, WGN, 3>(p);
+}
+// d2tile3 as a persistent grid of one workgroup per CU (launch_d2tile3p)
+template <int BM, int BN, int WGM, int WGN, int MF>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tile3p_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 3, MF, true, true>(p);
 }
 
 
@@ -1949,6 +2002,26 @@ hipError_t launch_ktile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
   hipLaunchKernelGGL((ktile_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
                      dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+// Compute units of the current device, read once per process (the persistent
+// grids launch one workgroup per CU).
+inline int device_cu_count() {
+  static const int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    return v;
+  }();
+  return cus;
+}
+template <int BM, int BN, int WGM, int WGN, int MF>
+hipError_t launch_d2tile3p(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t g = tiles < device_cu_count() ? tiles : device_cu_count();
+  hipLaunchKernelGGL((d2tile3p_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g), dim3(64 * WGM * WGN),
+                     0, s, a);
   return hipGetLastError();
 }
 template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>

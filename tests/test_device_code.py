@@ -57,6 +57,10 @@ def mangled(name):
         bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg15ktile_ns_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
                 f"ELi{sb}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"d2tile3p_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
+    if m:
+        bm, bn, wm, wn, mf = m.groups()
+        return f"_ZN4mihg15d2tile3p_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"d2tile3_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)_noxor", name)
     if m:
         bm, bn, wm, wn, mf = m.groups()

@@ -94,6 +94,31 @@ def test_every_instance_small_shapes(lib, small_cases, kidx):
                 check_tolerance(got, ref, what)
 
 
+PERSISTENT = [n for n in mh.kernel_names() if n.startswith("d2tile3p_")]
+
+
+@pytest.mark.parametrize("kernel", PERSISTENT)
+@pytest.mark.parametrize("M,N,K,kind", [(4400, 4400, 200, "int"), (8192, 4352, 64, "randn"),
+                                        (4352, 4400, 1000, "randn")])
+def test_persistent_grid_walks_every_tile(lib, kernel, M, N, K, kind):
+    """The persistent instance launches one workgroup per CU, and each walks
+    several output tiles.  These shapes have 289-544 tiles of 256x256 against
+    256 CUs, with ragged edges in M, N and K (200, 1000 are not multiples of
+    64), so most workgroups carry a second or third tile through the
+    prologue-overlapped transition.  Checked in full against the oracle."""
+    A, Bt = rand_problem(M, N, K, kind, seed=M + N + K)
+    log(f"persistent {kernel} {M}x{N}x{K} {kind}")
+    full = padded_out(M, N)
+    got = host(lib.run_kernel(kernel, gpu(A), gpu(Bt), full, group_m=4, xcd_remap=1))
+    ref = oracle.hgemm_tn(A, Bt)
+    if kind == "int":
+        check_bitexact(got, ref, f"{kernel} {M}x{N}x{K}")
+    else:
+        check_tolerance(got, ref, f"{kernel} {M}x{N}x{K}")
+    again = host(lib.run_kernel(kernel, gpu(A), gpu(Bt), padded_out(M, N), group_m=4, xcd_remap=1))
+    assert np.array_equal(got.view(np.uint16), again.view(np.uint16)), "repeat differs"
+
+
 def test_tiny_config_full(lib):
     p = inputs.tiny()
     A, Bt = inputs.make(p)
