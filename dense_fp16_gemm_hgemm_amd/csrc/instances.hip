@@ -114,6 +114,12 @@ namespace mihg {
 // spills it.
 #define MIHG_D2TILE3P_INSTANCES(X) \
   X(256, 256, 2, 4, 16)
+// C staged through LDS for whole-line stores (the "_sc" instances)
+#define MIHG_D2TILE3SC_INSTANCES(X) \
+  X(256, 256, 2, 4)                 \
+  X(256, 256, 2, 2)
+#define MIHG_D2TILESC_INSTANCES(X) \
+  X(128, 128, 2, 2)
 #define MIHG_KTILE_NS_B_INSTANCES(X) \
   X(128, 128, 2, 4, 128, 3, 2)
 
@@ -182,6 +188,10 @@ namespace mihg {
   template __global__ void d2tile3_ns_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
 #define INSTANTIATE_D2TILE3P(BM, BN, WGM, WGN, MF) \
   template __global__ void d2tile3p_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
+#define INSTANTIATE_D2TILE3SC(BM, BN, WGM, WGN) \
+  template __global__ void d2tile3sc_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_D2TILESC(BM, BN, WGM, WGN) \
+  template __global__ void d2tilesc_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_KTILE_NS_B(BM, BN, WGM, WGN, BK, S, SB) \
   template __global__ void ktile_ns_kernel<BM, BN, WGM, WGN, BK / 64, S, SB>(GemmArgs);
 #define INSTANTIATE_I8_D2TILE(BM, BN, WGM, WGN) \
@@ -203,6 +213,8 @@ MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
 MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
 MIHG_D2TILE3_NS_INSTANCES(INSTANTIATE_D2TILE3_NS)
 MIHG_D2TILE3P_INSTANCES(INSTANTIATE_D2TILE3P)
+MIHG_D2TILE3SC_INSTANCES(INSTANTIATE_D2TILE3SC)
+MIHG_D2TILESC_INSTANCES(INSTANTIATE_D2TILESC)
 MIHG_KTILE_NS_B_INSTANCES(INSTANTIATE_KTILE_NS_B)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
@@ -260,6 +272,13 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
   {"d2tile3p_" #BM "x" #BN "_w" #WGM "x" #WGN "_m" #MF, FAMILY_TILE, BM, BN, 64, WGM * WGN, MF, \
    1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3p<BM, BN, WGM, WGN, MF>,             \
    &grid_tile<BM, BN>},
+#define D2TILE3SC_DESC(BM, BN, WGM, WGN)                                                    \
+  {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16_sc", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16,  \
+   1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3sc<BM, BN, WGM, WGN>,              \
+   &grid_tile<BM, BN>},
+#define D2TILESC_DESC(BM, BN, WGM, WGN)                                                     \
+  {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16_sc", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16,   \
+   1, 1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tilesc<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
 #define KTILE_NS_B_DESC(BM, BN, WGM, WGN, BK, S, SB)                                          \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "b" #SB "_noxor", FAMILY_TILE, BM, \
    BN, BK, WGM * WGN, 16, 1, 1, (S * BM + SB * BN) * BK * 2, 1,                                 \
@@ -294,6 +313,8 @@ const KernelDesc kKernels[] = {
     MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)
     MIHG_D2TILE3_NS_INSTANCES(D2TILE3_NS_DESC)
     MIHG_D2TILE3P_INSTANCES(D2TILE3P_DESC)
+    MIHG_D2TILE3SC_INSTANCES(D2TILE3SC_DESC)
+    MIHG_D2TILESC_INSTANCES(D2TILESC_DESC)
     MIHG_KTILE_NS_B_INSTANCES(KTILE_NS_B_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
     // int8 variant: element-wise instance first, then the vector-load tiles

@@ -887,8 +887,11 @@ __device__ inline int ntiles_of(int tiles_m, int tiles_n) { return tiles_m * til
 // blockIdx.x + gridDim.x, ...; after a tile's last trip the next tile's first
 // copies are issued before this tile's last MFMAs and C stores, so their
 // latency hides behind that work instead of opening every tile.
+// SC = true stages each wave's C through LDS, 16 rows at a time, so that every
+// store instruction writes whole 128-byte row segments (16 bytes a lane)
+// instead of 32-byte pieces of 16 rows (8 bytes a lane from the MFMA layout).
 template <typename Op, int BM, int BN, int WGM, int WGN, int SA, int MF = 16, bool XS = true,
-          bool PERSIST = false>
+          bool PERSIST = false, bool SC = false>
 __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<MF>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -1135,7 +1138,51 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // g * (256 / MF) + 4 * (l / MF) + e for g < NACC / 4, e < 4
   char* Cw = static_cast<char*>(p.C) + em0 * ldc * CB;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - em0) * ldc * CB));
-  if ((N & 3) == 0) {
+  bool staged = false;
+  if constexpr (SC) {
+    static_assert(CB == 2 && MF == 16, "staged epilogue: binary16 C, 16x16 blocks");
+    // Each wave owns a private scratch of 16 rows x WTN halves: in A stage 2
+    // with three A stages (the next tile's first copies never target it),
+    // else at the start of the ring.  16-byte chunks are XORed with row & 7.
+    constexpr int SCR_OFF = SA == 3 ? 2 * A_STRIDE : 0;
+    constexpr int SCR_HALVES = 16 * WTN;
+    static_assert(NW * SCR_HALVES <= (SA == 3 ? A_STRIDE : LDS_HALVES), "staging scratch fits");
+    constexpr int CPRW = WTN / 8;        // 16-byte chunks per scratch row
+    constexpr int RPI = 64 / CPRW;       // scratch rows per 1 KiB read
+    if ((N & 7) == 0) {
+      staged = true;
+      // every wave's copies past the last K tile have landed (one may target
+      // the scratch rows) before any wave writes its scratch
+      __syncthreads();
+      _Float16* scr = lds + SCR_OFF + wave_u * SCR_HALVES;
+      const int srow = lane % 16, squad = lane / 16;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          h4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
+          const int col = fn * MF + 4 * squad;  // in halves, within the wave's columns
+          const int ch = (col >> 3) ^ (srow & 7);
+          *reinterpret_cast<h4*>(scr + srow * WTN + ch * 8 + (col & 7)) = o;
+        }
+        // one wave's LDS writes and reads complete in order: the reads below
+        // see the writes above, and the next fm's writes follow these reads
+#pragma unroll
+        for (int q = 0; q < 16 / RPI; ++q) {
+          const int r = q * RPI + lane / CPRW, c = lane % CPRW;
+          const h8 x = *reinterpret_cast<const h8*>(scr + r * WTN + ((c ^ (r & 7)) * 8));
+          const int i = wm * WTM + fm * MF + r;
+          const int j = en0 + wn * WTN + c * 8;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc,
+                                                 j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, 0, 0);
+        }
+      }
+    }
+  }
+  if (staged) {
+  } else if ((N & 3) == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int i = wm * WTM + fm * MF + lane % MF;
@@ -1190,6 +1237,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) i8_d2tile3_kernel(GemmArgs p) 
 template <int BM, int BN, int WGM, int WGN, int MF>
 __global__ void __launch_bounds__(64 * WGM * WGN) d2tile3p_kernel(GemmArgs p) {
   d2tile_body<OpF16, BM, BN, WGM, WGN, 3, MF, true, true>(p);
+}
+// C staged through LDS for whole-line stores (d2tile_body's SC)
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tile3sc_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 3, 16, true, false, true>(p);
+}
+template <int BM, int BN, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) d2tilesc_kernel(GemmArgs p) {
+  d2tile_body<OpF16, BM, BN, WGM, WGN, 2, 16, true, false, true>(p);
 }
 
 
@@ -2022,6 +2078,19 @@ hipError_t launch_d2tile3p(const GemmArgs& a, hipStream_t s) {
   const int64_t g = tiles < device_cu_count() ? tiles : device_cu_count();
   hipLaunchKernelGGL((d2tile3p_kernel<BM, BN, WGM, WGN, MF>), dim3((unsigned)g), dim3(64 * WGM * WGN),
                      0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_d2tile3sc(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((d2tile3sc_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g), dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN, int WGM, int WGN>
+hipError_t launch_d2tilesc(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((d2tilesc_kernel<BM, BN, WGM, WGN>), dim3((unsigned)g), dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>

@@ -178,9 +178,8 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
 // still fills a good part of the machine ([P2] 正文 paragraph 3: large tiles
 // raise reuse and lower occupancy), else a K split.  The thresholds come from
 // timing every instance over the LLM projection and square shapes on MI355X:
-//  - from three waves of 256x256 tiles up, the persistent form (one workgroup
-//    per CU walks its tiles, the next tile's first copies overlapping this
-//    tile's last MFMAs and stores) is 2-4% ahead;
+//  - the binary16 picks stage C through LDS ("_sc"): whole-line stores make
+//    short-K shapes up to 1.4x faster and cost nothing at long K;
 //  - one partial wave of 256x256 tiles beats more waves of smaller tiles down
 //    to three quarters of a wave (the chip is power-bound: idle CUs buy clock
 //    for the busy ones);
@@ -214,7 +213,7 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   };
   // the int8 instances with the same tiles and a K step of the same bytes
   const bool i8 = dtype == mihg::DTYPE_I8;
-  const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16");
+  const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16_sc");
   const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2");
   // When the output is one row of tiles B is streamed through once: those
   // tiles copy it with the non-temporal policy ("_nt"), which
@@ -226,11 +225,8 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   const int k32 = find_kernel(i8 ? (M <= 32 ? "i8_ktile_32x64_w2x2_k256_s3_nt" : "i8_ktile_32x64_w2x2_k256_s3")
                                  : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3"));
   const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3_nt" : "ktile_16x64_w1x4_k128_s3_nt");
-  const int k128d = find_kernel(i8 ? "i8_d2tile_128x128_w2x2_m16" : "d2tile_128x128_w2x2_m16");
-  const int k256p = i8 ? -1 : find_kernel("d2tile3p_256x256_w2x4_m16");
-  if (M > 64 && k256p >= 0 && tiles(k256p) >= 768) {
-    pick(k256p, 1, 0, 1);
-  } else if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
+  const int k128d = find_kernel(i8 ? "i8_d2tile_128x128_w2x2_m16" : "d2tile_128x128_w2x2_m16_sc");
+  if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
     pick(k256, 8, 1, 1);
   } else if (M > 64 && k128d >= 0 && tiles(k128d) >= 512) {
     pick(k128d, 8, 1, 1);

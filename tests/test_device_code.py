@@ -57,6 +57,11 @@ def mangled(name):
         bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg15ktile_ns_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
                 f"ELi{sb}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"(d2tile3p|d2tile3|d2tile)_(\d+)x(\d+)_w(\d+)x(\d+)_m16_sc", name)
+    if m:
+        kind, bm, bn, wm, wn = m.groups()
+        kname = {"d2tile3p": "d2tile3psc", "d2tile3": "d2tile3sc", "d2tile": "d2tilesc"}[kind]
+        return f"_ZN4mihg{len(kname) + 7}{kname}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"d2tile3p_(\d+)x(\d+)_w(\d+)x(\d+)_m(\d+)", name)
     if m:
         bm, bn, wm, wn, mf = m.groups()

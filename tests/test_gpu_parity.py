@@ -94,10 +94,10 @@ def test_every_instance_small_shapes(lib, small_cases, kidx):
                 check_tolerance(got, ref, what)
 
 
-PERSISTENT = [n for n in mh.kernel_names() if n.startswith("d2tile3p_")]
+LARGE_VARIANTS = [n for n in mh.kernel_names() if n.startswith("d2tile3p_") or n.endswith("_sc")]
 
 
-@pytest.mark.parametrize("kernel", PERSISTENT)
+@pytest.mark.parametrize("kernel", LARGE_VARIANTS)
 @pytest.mark.parametrize("M,N,K,kind", [(4400, 4400, 200, "int"), (8192, 4352, 64, "randn"),
                                         (4352, 4400, 1000, "randn")])
 def test_persistent_grid_walks_every_tile(lib, kernel, M, N, K, kind):
@@ -105,7 +105,9 @@ def test_persistent_grid_walks_every_tile(lib, kernel, M, N, K, kind):
     several output tiles.  These shapes have 289-544 tiles of 256x256 against
     256 CUs, with ragged edges in M, N and K (200, 1000 are not multiples of
     64), so most workgroups carry a second or third tile through the
-    prologue-overlapped transition.  Checked in full against the oracle."""
+    prologue-overlapped transition.  The same shapes check the instances that
+    stage C through LDS ("_sc") over many tiles and ragged edges.  Checked in
+    full against the oracle."""
     A, Bt = rand_problem(M, N, K, kind, seed=M + N + K)
     log(f"persistent {kernel} {M}x{N}x{K} {kind}")
     full = padded_out(M, N)
