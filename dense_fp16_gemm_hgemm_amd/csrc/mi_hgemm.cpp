@@ -657,11 +657,15 @@ struct TimingStream {
 // Capture `reps` launches of one candidate on stream `ts` into a graph and
 // time 5 replays; appends microseconds per launch to `trials`.
 // The timing operands: nsets copies of (A, B) back to back, set i at
-// base + i * (M + N) * K elements of eb bytes (A first).
+// base + i * (M + N) * K elements of eb bytes (A first), and nsets outputs C,
+// output i at cbase + i * cstride bytes.
 struct TimingSets {
   char* base = nullptr;
+  char* cbase = nullptr;
+  int64_t cstride = 0;
   int nsets = 1;
   int eb = 2;
+  void* C(int i) const { return cbase + (int64_t)i * cstride; }
   const void* A(int64_t M, int64_t N, int64_t K, int i) const {
     return base + ((int64_t)i * (M + N) * K) * eb;
   }
@@ -671,11 +675,12 @@ struct TimingSets {
 };
 
 // Capture `reps` launches of one candidate on stream `ts` into a graph (launch r
-// reads timing set r mod nsets, so that together they overflow the MALL and
-// each launch reads its operands from HBM, as in real use) and time 5 replays;
+// reads timing set r mod nsets and writes its output, so that together they
+// overflow the MALL and each launch reads its operands from HBM and writes C
+// past the MALL, as in real use) and time 5 replays;
 // appends microseconds per launch to `trials`.
 hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t N, int64_t K,
-                        const TimingSets& sets, void* C, int64_t ldc, int reps,
+                        const TimingSets& sets, int64_t ldc, int reps,
                         hipStream_t ts, hipEvent_t ev0, hipEvent_t ev1,
                         std::vector<double>& trials) {
   hipGraph_t graph = nullptr;
@@ -685,7 +690,7 @@ hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t 
   mi_hgemm_status_t st = MI_HGEMM_OK;
   for (int r = 0; r < reps && st == MI_HGEMM_OK; ++r)
     st = launch(h, cand, M, N, K, sets.A(M, N, K, r % sets.nsets), K, sets.B(M, N, K, r % sets.nsets),
-                K, C, ldc, ts);
+                K, sets.C(r % sets.nsets), ldc, ts);
   e = hipStreamEndCapture(ts, &graph);
   if (e == hipSuccess && st != MI_HGEMM_OK) e = hipErrorLaunchFailure;
   if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -728,12 +733,14 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
 
   // a, b: small integers (fp16) or uniform int8, for the bit-exact check.
   // Timing sets: random mantissas scaled by 1/sqrt(K) (the clock depends on the
-  // data), or uniform int8, in as many copies as make 2.2x the 256 MiB MALL (at
-  // most 64 copies and 4 GiB), so that the timed launches read their operands
-  // from HBM.
-  Scratch a, b, tsets, c, cref, cnt;
+  // data), or uniform int8, each with its own output, in as many copies as make
+  // 2.2x the 256 MiB MALL (at most 64 copies and 4 GiB), so that the timed
+  // launches read their operands from HBM and write C as in real use (one
+  // output shared by every launch would stay in the MALL and flatter the
+  // store-heavy candidates).
+  Scratch a, b, tsets, tcs, c, cref, cnt;
   hipError_t e;
-  const double set_bytes = (double)(M + N) * K * eb;
+  const double set_bytes = (double)(M + N) * K * eb + (double)M * ldc * cb;
   TimingSets sets;
   sets.eb = eb;
   sets.nsets = (int)std::max(1.0, std::min({64.0, std::ceil(2.2 * 256.0 * 1048576.0 / set_bytes),
@@ -743,6 +750,9 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   if ((e = hipMalloc(&tsets.p, (size_t)sets.nsets * (M + N) * K * eb)) != hipSuccess)
     return hip_fail(h, e);
   sets.base = static_cast<char*>(tsets.p);
+  sets.cstride = M * ldc * cb;
+  if ((e = hipMalloc(&tcs.p, (size_t)sets.nsets * sets.cstride)) != hipSuccess) return hip_fail(h, e);
+  sets.cbase = static_cast<char*>(tcs.p);
   if ((e = hipMalloc(&c.p, (size_t)M * ldc * cb)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cref.p, (size_t)M * ldc * cb)) != hipSuccess) return hip_fail(h, e);
   if ((e = hipMalloc(&cnt.p, sizeof(int))) != hipSuccess) return hip_fail(h, e);
@@ -872,7 +882,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     const int reps = (int)std::max((double)sets.nsets,
                                    std::min(200.0, std::ceil(1.0 / std::max(1e-4, (double)ms))));
     std::vector<double> trials;
-    e = time_replays(h, cand, M, N, K, sets, c.p, ldc, reps, ts.s, ev0, ev1, trials);
+    e = time_replays(h, cand, M, N, K, sets, ldc, reps, ts.s, ev0, ev1, trials);
     if (e != hipSuccess) {
       result = hip_fail(h, e);
       break;

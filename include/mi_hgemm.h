@@ -148,9 +148,9 @@ mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int
  * discarded); it is then timed on operands with random mantissas scaled by
  * 1/sqrt(K) (the clock under load depends on the data), as the median of 5
  * replays of a captured graph of repeated launches on a private stream.  The
- * launches rotate over enough operand copies to overflow the 256 MiB MALL
- * (at most 64 copies and 4 GiB), so each reads its operands from HBM as in
- * real use.  The fastest correct one becomes the handle's entry for the shape.
+ * launches rotate over enough copies of the operands and of the output to
+ * overflow the 256 MiB MALL (at most 64 copies and 4 GiB), so each reads its
+ * operands from HBM and writes its C past the MALL, as in real use.  The fastest correct one becomes the handle's entry for the shape.
  * With MI_HGEMM_TUNE_PERSIST the entry is appended to the handle's table file.
  * With MI_HGEMM_TUNE_INT8 the int8 instances are searched instead (K a
  * multiple of 16 and at most 131071); their check and timing operands are
