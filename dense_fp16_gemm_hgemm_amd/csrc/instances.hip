@@ -118,6 +118,11 @@ namespace mihg {
 #define MIHG_D2TILE3SC_INSTANCES(X) \
   X(256, 256, 2, 4)                 \
   X(256, 256, 2, 2)
+#define MIHG_KTILESC_INSTANCES(X) \
+  X(128, 128, 2, 4, 128, 3, 2)     \
+  X(128, 128, 2, 2, 128, 3, 2)     \
+  X(64, 64, 2, 2, 128, 3, 3)       \
+  X(32, 64, 2, 2, 128, 3, 3)
 #define MIHG_D2TILESC_INSTANCES(X) \
   X(128, 128, 2, 2)
 #define MIHG_KTILE_NS_B_INSTANCES(X) \
@@ -190,6 +195,8 @@ namespace mihg {
   template __global__ void d2tile3p_kernel<BM, BN, WGM, WGN, MF>(GemmArgs);
 #define INSTANTIATE_D2TILE3SC(BM, BN, WGM, WGN) \
   template __global__ void d2tile3sc_kernel<BM, BN, WGM, WGN>(GemmArgs);
+#define INSTANTIATE_KTILESC(BM, BN, WGM, WGN, BK, S, SB) \
+  template __global__ void ktilesc_kernel<BM, BN, WGM, WGN, BK / 64, S, SB>(GemmArgs);
 #define INSTANTIATE_D2TILESC(BM, BN, WGM, WGN) \
   template __global__ void d2tilesc_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_KTILE_NS_B(BM, BN, WGM, WGN, BK, S, SB) \
@@ -215,6 +222,7 @@ MIHG_D2TILE3_NS_INSTANCES(INSTANTIATE_D2TILE3_NS)
 MIHG_D2TILE3P_INSTANCES(INSTANTIATE_D2TILE3P)
 MIHG_D2TILE3SC_INSTANCES(INSTANTIATE_D2TILE3SC)
 MIHG_D2TILESC_INSTANCES(INSTANTIATE_D2TILESC)
+MIHG_KTILESC_INSTANCES(INSTANTIATE_KTILESC)
 MIHG_KTILE_NS_B_INSTANCES(INSTANTIATE_KTILE_NS_B)
 MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
@@ -276,6 +284,10 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
   {"d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16_sc", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16,  \
    1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_d2tile3sc<BM, BN, WGM, WGN>,              \
    &grid_tile<BM, BN>},
+#define KTILESC_DESC(BM, BN, WGM, WGN, BK, S, SB)                                              \
+  {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S "b" #SB "_sc", FAMILY_TILE, BM, BN,  \
+   BK, WGM * WGN, 16, 1, 1, (S * BM + SB * BN) * BK * 2, 1,                                     \
+   &launch_ktilesc<BM, BN, WGM, WGN, BK / 64, S, SB>, &grid_tile<BM, BN>},
 #define D2TILESC_DESC(BM, BN, WGM, WGN)                                                     \
   {"d2tile_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16_sc", FAMILY_TILE, BM, BN, 64, WGM * WGN, 16,   \
    1, 1, 2 * (BM + BN) * kD2Row * 2, 0, &launch_d2tilesc<BM, BN, WGM, WGN>, &grid_tile<BM, BN>},
@@ -315,6 +327,7 @@ const KernelDesc kKernels[] = {
     MIHG_D2TILE3P_INSTANCES(D2TILE3P_DESC)
     MIHG_D2TILE3SC_INSTANCES(D2TILE3SC_DESC)
     MIHG_D2TILESC_INSTANCES(D2TILESC_DESC)
+    MIHG_KTILESC_INSTANCES(KTILESC_DESC)
     MIHG_KTILE_NS_B_INSTANCES(KTILE_NS_B_DESC)
     MIHG_SKINNY_INSTANCES(SKINNY_DESC)
     // int8 variant: element-wise instance first, then the vector-load tiles

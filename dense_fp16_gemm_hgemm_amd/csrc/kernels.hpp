@@ -887,6 +887,47 @@ __device__ inline int ntiles_of(int tiles_m, int tiles_n) { return tiles_m * til
 // blockIdx.x + gridDim.x, ...; after a tile's last trip the next tile's first
 // copies are issued before this tile's last MFMAs and C stores, so their
 // latency hides behind that work instead of opening every tile.
+// Staged C store (the "_sc" instances): one wave's FM x FN blocks of 16x16
+// fp32 results go to binary16 through a private LDS scratch of 16 rows x WTN
+// halves, one 16-row slice at a time, and are stored as 16-byte row chunks
+// (whole row segments of the wave's columns) instead of 8-byte pieces of 16
+// rows.  The scratch's 16-byte chunks are XORed with the row's low bits.  One
+// wave's LDS writes and reads complete in order, so a slice needs no barrier.
+// row0: the wave's first row within the tile; col0: its first column of C;
+// rsc covers the tile's rows; columns at or past N are dropped (N % 8 == 0).
+// (d2tile_body inlines the same steps: through this helper its 4-wave 256x256
+// form, which uses every register, spilled one value.)
+template <int FM, int FN, int WTN, typename Acc>
+__device__ __forceinline__ void store_c_staged(const Acc (&acc)[FM][FN], _Float16* scr,
+                                               __amdgpu_buffer_rsrc_t rsc, int row0, int col0,
+                                               int N, int64_t ldc, int lane) {
+  constexpr int CPRW = WTN / 8;                  // 16-byte chunks per scratch row
+  constexpr int SWM = CPRW >= 8 ? 7 : CPRW - 1;  // XOR mask of the chunk index
+  static_assert(CPRW % 4 == 0 && (CPRW & (CPRW - 1)) == 0, "power-of-two rows of >= 4 chunks");
+  const int srow = lane % 16, squad = lane / 16;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      h4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (_Float16)acc[fm][fn][e];
+      const int col = fn * 16 + 4 * squad;  // in halves, within the wave's columns
+      const int ch = (col >> 3) ^ (srow & SWM);
+      *reinterpret_cast<h4*>(scr + srow * WTN + ch * 8 + (col & 7)) = o;
+    }
+#pragma unroll
+    for (int q = 0; q < 16 * CPRW / 64; ++q) {
+      const int idx = q * 64 + lane, r = idx / CPRW, c = idx % CPRW;
+      const h8 x = *reinterpret_cast<const h8*>(scr + r * WTN + ((c ^ (r & SWM)) * 8));
+      const int i = row0 + fm * 16 + r;
+      const int j = col0 + c * 8;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc,
+                                             j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, 0, 0);
+    }
+  }
+}
+
 // SC = true stages each wave's C through LDS, 16 rows at a time, so that every
 // store instruction writes whole 128-byte row segments (16 bytes a lane)
 // instead of 32-byte pieces of 16 rows (8 bytes a lane from the MFMA layout).
@@ -1467,7 +1508,7 @@ pptile_kernel(GemmArgs p) {
 // chunk l % (8*KB), and so loads logical chunk (l % (8*KB)) ^ (row & 15).
 // XS = false: unswizzled rows, the "no swizzle" candidate (as in d2tile_body)
 template <typename Op, int BM, int BN, int WGM, int WGN, int KB, int S, int SB = S, bool B_NT = false,
-          bool XS = true>
+          bool XS = true, bool SC = false>
 __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   using MM = typename Op::template Mma<16>;
   constexpr int EB = Op::kEB, CB = Op::kCB;
@@ -1679,7 +1720,20 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
 
   char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
-  if ((N & 3) == 0) {
+  bool staged = false;
+  if constexpr (SC) {
+    static_assert(CB == 2, "staged epilogue: binary16 C");
+    static_assert(NW * 16 * WTN <= LDS_HALVES, "staging scratch fits");
+    if ((N & 7) == 0) {
+      staged = true;
+      // every wave is done with the ring (and with the split-K flag word)
+      __syncthreads();
+      store_c_staged<FM, FN, WTN>(acc, lds + wave_u * (16 * WTN), rsc, wm * WTM, n0 + wn * WTN, N,
+                                  ldc, lane);
+    }
+  }
+  if (staged) {
+  } else if ((N & 3) == 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int i = wm * WTM + fm * MF + lane % MF;
@@ -1720,6 +1774,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) d2tile3_ns_kernel(GemmArgs p) 
 template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
 __global__ void __launch_bounds__(64 * WGM * WGN) ktile_ns_kernel(GemmArgs p) {
   ktile_body<OpF16, BM, BN, WGM, WGN, KB, S, SB, false, false>(p);
+}
+// C staged through LDS for whole row-segment stores
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
+__global__ void __launch_bounds__(64 * WGM * WGN) ktilesc_kernel(GemmArgs p) {
+  ktile_body<OpF16, BM, BN, WGM, WGN, KB, S, SB, false, true, true>(p);
 }
 // B copied with the non-temporal policy (a tuner candidate for few tile rows)
 template <int BM, int BN, int WGM, int WGN, int KB, int S>
@@ -2081,6 +2140,13 @@ hipError_t launch_d2tile3p(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WGM, int WGN, int KB, int S, int SB>
+hipError_t launch_ktilesc(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.splitk;
+  hipLaunchKernelGGL((ktilesc_kernel<BM, BN, WGM, WGN, KB, S, SB>), dim3((unsigned)g),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
 template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_d2tile3sc(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);

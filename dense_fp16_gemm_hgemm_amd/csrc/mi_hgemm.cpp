@@ -178,8 +178,8 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
 // still fills a good part of the machine ([P2] 正文 paragraph 3: large tiles
 // raise reuse and lower occupancy), else a K split.  The thresholds come from
 // timing every instance over the LLM projection and square shapes on MI355X:
-//  - the binary16 picks stage C through LDS ("_sc"): whole-line stores make
-//    short-K shapes up to 1.4x faster and cost nothing at long K;
+//  - the binary16 picks stage C through LDS ("_sc"): whole row-segment stores
+//    make short-K shapes up to 1.2-1.3x faster and cost nothing at long K;
 //  - one partial wave of 256x256 tiles beats more waves of smaller tiles down
 //    to three quarters of a wave (the chip is power-bound: idle CUs buy clock
 //    for the busy ones);
@@ -214,16 +214,16 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   // the int8 instances with the same tiles and a K step of the same bytes
   const bool i8 = dtype == mihg::DTYPE_I8;
   const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16_sc");
-  const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2");
+  const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2_sc");
   // When the output is one row of tiles B is streamed through once: those
   // tiles copy it with the non-temporal policy ("_nt"), which
   // leaves the caches to A (measured 1-10% faster on the 16- and 64-row
   // projection shapes).
   const bool one_row = M <= 64;
   const int k64 = find_kernel(i8 ? (one_row ? "i8_ktile_64x64_w2x2_k256_s3_nt" : "i8_ktile_64x64_w2x2_k256_s3")
-                                 : (one_row ? "ktile_64x64_w2x2_k128_s3_nt" : "ktile_64x64_w2x2_k128_s3"));
+                                 : (one_row ? "ktile_64x64_w2x2_k128_s3_nt" : "ktile_64x64_w2x2_k128_s3b3_sc"));
   const int k32 = find_kernel(i8 ? (M <= 32 ? "i8_ktile_32x64_w2x2_k256_s3_nt" : "i8_ktile_32x64_w2x2_k256_s3")
-                                 : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3"));
+                                 : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3b3_sc"));
   const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3_nt" : "ktile_16x64_w1x4_k128_s3_nt");
   const int k128d = find_kernel(i8 ? "i8_d2tile_128x128_w2x2_m16" : "d2tile_128x128_w2x2_m16_sc");
   if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {

@@ -158,16 +158,16 @@ def test_heuristic_picks_by_shape(inspect_handle):
     assert choice(2048, 4096, 4096) == ("d2tile_128x128_w2x2_m16_sc", 1)
     assert choice(4096, 2048, 8192) == ("d2tile_128x128_w2x2_m16_sc", 1)
     # then deep-K 128x128 tiles while there are 128 of them
-    assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
-    assert choice(256, 11008, 4096) == ("ktile_128x128_w2x4_k128_s3b2", 1)
+    assert choice(1024, 4096, 4096) == ("ktile_128x128_w2x4_k128_s3b2_sc", 1)
+    assert choice(256, 11008, 4096) == ("ktile_128x128_w2x4_k128_s3b2_sc", 1)
     # then 64x64, split over K when the tiles are few and K is long; when the
     # output is one row of tiles B is streamed once and copied non-temporally
-    assert choice(256, 4096, 4096) == ("ktile_64x64_w2x2_k128_s3", 1)
+    assert choice(256, 4096, 4096) == ("ktile_64x64_w2x2_k128_s3b3_sc", 1)
     assert choice(64, 11008, 4096) == ("ktile_64x64_w2x2_k128_s3_nt", 1)
     assert choice(64, 4096, 11008) == ("ktile_64x64_w2x2_k128_s3_nt", 4)
     # M <= 64 over a short K: 32x64 tiles, split to fill the device (two rows
     # of tiles read B twice: the cached copy)
-    assert choice(64, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3", 2)
+    assert choice(64, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3b3_sc", 2)
     assert choice(32, 4096, 4096) == ("ktile_32x64_w2x2_k128_s3_nt", 4)
     # 16 rows: 16x64 deep-K tiles for wide or deep shapes, skinny otherwise
     assert choice(16, 14336, 4096) == ("ktile_16x64_w1x4_k128_s3_nt", 1)

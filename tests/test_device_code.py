@@ -57,6 +57,11 @@ def mangled(name):
         bm, bn, wm, wn, bk, s, sb = m.groups()
         return (f"_ZN4mihg15ktile_ns_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
                 f"ELi{sb}EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)b(\d+)_sc", name)
+    if m:
+        bm, bn, wm, wn, bk, s, sb = m.groups()
+        return (f"_ZN4mihg14ktilesc_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{int(bk) // 64}ELi{s}"
+                f"ELi{sb}EEEvNS_8GemmArgsE")
     m = re.fullmatch(r"(d2tile3p|d2tile3|d2tile)_(\d+)x(\d+)_w(\d+)x(\d+)_m16_sc", name)
     if m:
         kind, bm, bn, wm, wn = m.groups()

@@ -333,7 +333,8 @@ SPLIT_KERNELS = ["dtile_128x128_w2x2_m16_s4", "dtile_256x128_w2x2_m16_s4",
                  "skinny_4x1_w8_u2", "ktile_16x64_w1x4_k256_s3", "ktile_64x64_w2x2_k128_s3",
                  "ktile_128x128_w2x2_k128_s2", "ktile_128x128_w2x4_k128_s3b2",
                  "ktile_16x64_w1x4_k256_s3_nt", "ktile_64x64_w2x2_k128_s3_nt",
-                 "ktile_128x128_w2x4_k128_s3b2_noxor"]
+                 "ktile_128x128_w2x4_k128_s3b2_noxor", "ktile_128x128_w2x4_k128_s3b2_sc",
+                 "ktile_64x64_w2x2_k128_s3b3_sc"]
 
 
 @pytest.mark.parametrize("kernel", SPLIT_KERNELS)
