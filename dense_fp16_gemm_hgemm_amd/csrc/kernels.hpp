@@ -1197,6 +1197,9 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
       __syncthreads();
       _Float16* scr = lds + SCR_OFF + wave_u * SCR_HALVES;
       const int srow = lane % 16, squad = lane / 16;
+      // With K this short the launch is mostly C traffic: store it non-temporally
+      // so the output streams past the caches instead of evicting its own lines.
+      const bool c_nt = K <= 128;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -1216,8 +1219,11 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
           const h8 x = *reinterpret_cast<const h8*>(scr + r * WTN + ((c ^ (r & 7)) * 8));
           const int i = wm * WTM + fm * MF + r;
           const int j = en0 + wn * WTN + c * 8;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc,
-                                                 j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, 0, 0);
+          const uint32_t off = j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB;
+          if (c_nt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc, off, 0, 2);
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc, off, 0, 0);
         }
       }
     }
