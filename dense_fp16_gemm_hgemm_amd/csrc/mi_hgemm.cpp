@@ -28,6 +28,7 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/mi_hgemm.h"
@@ -70,6 +71,32 @@ struct Key {
   bool operator<(const Key& o) const {
     return std::tie(M, N, K, cls) < std::tie(o.M, o.N, o.K, o.cls);
   }
+  bool operator==(const Key& o) const {
+    return M == o.M && N == o.N && K == o.K && cls == o.cls;
+  }
+};
+
+struct KeyHash {
+  size_t operator()(const Key& k) const noexcept {
+    uint64_t h = (uint64_t)k.M * 0x9E3779B97F4A7C15ull;
+    h = (h ^ (uint64_t)k.N) * 0xBF58476D1CE4E5B9ull;
+    h = (h ^ (uint64_t)k.K) * 0x94D049BB133111EBull;
+    return (size_t)(h ^ (uint64_t)k.cls ^ (h >> 31));
+  }
+};
+
+// Resolved configs kept per handle (table hits, nearest-shape picks and
+// heuristic picks alike), so a repeated shape costs one hash lookup.  Cleared
+// when the table changes (tune) and when it reaches this many entries.
+constexpr size_t kMemoMax = 4096;
+
+// Where a launch's split-K partial tiles and per-tile arrival counters live,
+// and how much of each there is.
+struct Workspace {
+  float* ws = nullptr;
+  int* cnt = nullptr;
+  size_t ws_bytes = 0;
+  int64_t max_tiles = 0;
 };
 
 }  // namespace
@@ -83,6 +110,8 @@ struct mi_hgemm_ctx {
   std::string table_path;  // resolved path (may be empty)
   std::map<Key, Config> table;
   std::mutex mu;           // guards table updates (tune) and last_hip_error
+  std::unordered_map<Key, Config, KeyHash> memo;  // resolved dispatch, see kMemoMax
+  std::mutex memo_mu;      // guards memo (run/plan may be called from several threads)
 };
 
 namespace {
@@ -157,7 +186,7 @@ bool aligned_class(int32_t dtype, int64_t K, const void* A, int64_t lda, const v
 // the result may be smaller than asked (1 = no split).  -1 when the instance
 // cannot split or the partial tiles would not fit the workspace.
 int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, int requested,
-                        int64_t* chunk_out) {
+                        int64_t* chunk_out, size_t ws_bytes = kWsBytes, int64_t max_tiles = kMaxTiles) {
   if (requested <= 1) {
     *chunk_out = K;
     return 1;
@@ -168,8 +197,8 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
   *chunk_out = sk > 1 ? chunk : K;
   if (sk <= 1) return 1;
   const int64_t tiles = kd.grid((int32_t)M, (int32_t)N);
-  if (tiles > kMaxTiles || tiles * sk > INT32_MAX ||
-      (size_t)tiles * sk * kd.bm * kd.bn * sizeof(float) > kWsBytes)
+  if (tiles > max_tiles || tiles * sk > INT32_MAX ||
+      (size_t)tiles * sk * kd.bm * kd.bn * sizeof(float) > ws_bytes)
     return -1;
   return sk;
 }
@@ -257,7 +286,7 @@ Config checked(Config c, int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
-Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls) {
+Config select_uncached(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls) {
   const Key key{M, N, K, cls};
   auto it = h->table.find(key);
   if (it != h->table.end()) return checked(it->second, M, N, K);
@@ -276,6 +305,30 @@ Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls) {
   }
   if (pick) return checked(*pick, M, N, K);
   return heuristic(M, N, K, cls);
+}
+
+// Dispatch (a1): the exact table entry, else the nearest tuned shape, else the
+// heuristic -- resolved once per (M, N, K, class) and then looked up.
+// remember = false resolves a miss without storing it (no host allocation).
+Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls,
+              bool remember = true) {
+  const Key key{M, N, K, cls};
+  {
+    std::lock_guard<std::mutex> lk(h->memo_mu);
+    auto it = h->memo.find(key);
+    if (it != h->memo.end()) return it->second;
+  }
+  const Config c = select_uncached(h, M, N, K, cls);
+  if (!remember) return c;
+  std::lock_guard<std::mutex> lk(h->memo_mu);
+  if (h->memo.size() >= kMemoMax) h->memo.clear();
+  h->memo.emplace(key, c);
+  return c;
+}
+
+void forget_resolved(mi_hgemm_ctx* h) {
+  std::lock_guard<std::mutex> lk(h->memo_mu);
+  h->memo.clear();
 }
 
 // Table file: one entry per line,
@@ -372,9 +425,19 @@ struct DeviceGuard {
   }
 };
 
+// The handle's own split-K workspace.
+Workspace handle_ws(const mi_hgemm_ctx* h) {
+  Workspace w;
+  w.ws = h->ws;
+  w.cnt = h->cnt;
+  w.ws_bytes = h->ws ? kWsBytes : 0;
+  w.max_tiles = h->cnt ? kMaxTiles : 0;
+  return w;
+}
+
 mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N, int64_t K,
                          const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                         int64_t ldc, hipStream_t stream) {
+                         int64_t ldc, hipStream_t stream, const Workspace& w) {
   const KernelDesc& kd = kKernels[c.kernel];
   if (kd.grid((int32_t)M, (int32_t)N) > INT32_MAX) return MI_HGEMM_ERR_UNSUPPORTED;
   GemmArgs a;
@@ -391,12 +454,13 @@ mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N,
   a.xcd_remap = c.xcd ? 1 : 0;
   a.splitk = 1;
   a.kchunk = (int32_t)K;
-  a.ws = h->ws;
-  a.cnt = h->cnt;
+  a.ws = w.ws;
+  a.cnt = w.cnt;
   if (c.splitk > 1) {
-    if (!h->ws || !h->cnt) return MI_HGEMM_ERR_UNSUPPORTED;
+    if (!w.ws || !w.cnt) return MI_HGEMM_ERR_UNSUPPORTED;
     int64_t chunk = K;
-    const int64_t sk = effective_split(kd, M, N, K, c.splitk, &chunk);
+    // never more partial tiles or counters than the workspace holds
+    const int64_t sk = effective_split(kd, M, N, K, c.splitk, &chunk, w.ws_bytes, w.max_tiles);
     if (sk < 1) return MI_HGEMM_ERR_UNSUPPORTED;
     a.splitk = (int32_t)sk;
     a.kchunk = (int32_t)chunk;
@@ -408,7 +472,8 @@ mi_hgemm_status_t launch(mi_hgemm_ctx* h, const Config& c, int64_t M, int64_t N,
 
 mi_hgemm_status_t run_config(mi_hgemm_ctx* h, int32_t dtype, const Config& c, int64_t M,
                              int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                             int64_t ldb, void* C, int64_t ldc, void* stream) {
+                             int64_t ldb, void* C, int64_t ldc, void* stream,
+                             const Workspace& w) {
   if (M == 0 || N == 0) return MI_HGEMM_OK;
   if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
   DeviceGuard g(h->device);
@@ -422,7 +487,7 @@ mi_hgemm_status_t run_config(mi_hgemm_ctx* h, int32_t dtype, const Config& c, in
     const hipError_t e = mihg::launch_zero_fill(C, ldc * w, (int32_t)M, (int32_t)(N * w), s);
     return e == hipSuccess ? MI_HGEMM_OK : hip_fail(h, e);
   }
-  return launch(h, c, M, N, K, A, lda, B, ldb, C, ldc, s);
+  return launch(h, c, M, N, K, A, lda, B, ldb, C, ldc, s, w);
 }
 
 mi_hgemm_status_t plan_impl(mi_hgemm_ctx* h, int32_t dtype, int64_t M, int64_t N, int64_t K,
@@ -456,7 +521,7 @@ mi_hgemm_status_t run_impl(mi_hgemm_ctx* h, int32_t dtype, int64_t M, int64_t N,
   if (K > 0)
     c = select(h, M, N, K, make_cls(dtype, aligned_class(dtype, K, A, lda, B, ldb, C, ldc)));
   if (c.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
-  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream, handle_ws(h));
 }
 
 }  // namespace
@@ -608,7 +673,7 @@ mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
   c.group_m = group_m;
   c.xcd = xcd_remap;
   c.splitk = split_k;
-  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return run_config(h, dtype, c, M, N, K, A, lda, B, ldb, C, ldc, stream, handle_ws(h));
 }
 
 int mi_hgemm_table_size(mi_hgemm_handle_t h) {
@@ -690,7 +755,7 @@ hipError_t time_replays(mi_hgemm_ctx* h, const Config& cand, int64_t M, int64_t 
   mi_hgemm_status_t st = MI_HGEMM_OK;
   for (int r = 0; r < reps && st == MI_HGEMM_OK; ++r)
     st = launch(h, cand, M, N, K, sets.A(M, N, K, r % sets.nsets), K, sets.B(M, N, K, r % sets.nsets),
-                K, sets.C(r % sets.nsets), ldc, ts);
+                K, sets.C(r % sets.nsets), ldc, ts, handle_ws(h));
   e = hipStreamEndCapture(ts, &graph);
   if (e == hipSuccess && st != MI_HGEMM_OK) e = hipErrorLaunchFailure;
   if (e == hipSuccess) e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
@@ -774,7 +839,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   Config ref;
   ref.kernel = generic_kernel(dtype);
   if (ref.kernel < 0) return MI_HGEMM_ERR_UNSUPPORTED;
-  mi_hgemm_status_t st = launch(h, ref, M, N, K, a.p, K, b.p, K, cref.p, ldc, s);
+  mi_hgemm_status_t st = launch(h, ref, M, N, K, a.p, K, b.p, K, cref.p, ldc, s, handle_ws(h));
   if (st != MI_HGEMM_OK) return st;
 
   hipEvent_t ev0, ev1;
@@ -845,7 +910,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
   mi_hgemm_status_t result = MI_HGEMM_OK;
   for (const Config& cand : cands) {
     // correctness first: bit-identical to the reference on exact integer data
-    st = launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s);
+    st = launch(h, cand, M, N, K, a.p, K, b.p, K, c.p, ldc, s, handle_ws(h));
     if (st != MI_HGEMM_OK) {
       result = st;
       break;
@@ -871,7 +936,8 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     // than host launch cost; the median of 5 replays is kept
     float ms = 0.f;
     (void)hipEventRecord(ev0, s);
-    (void)launch(h, cand, M, N, K, sets.A(M, N, K, 0), K, sets.B(M, N, K, 0), K, c.p, ldc, s);
+    (void)launch(h, cand, M, N, K, sets.A(M, N, K, 0), K, sets.B(M, N, K, 0), K, c.p, ldc, s,
+                 handle_ws(h));
     (void)hipEventRecord(ev1, s);
     if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
       result = hip_fail(h, e);
@@ -908,6 +974,7 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     std::lock_guard<std::mutex> lk(h->mu);
     h->table[key] = best;
   }
+  forget_resolved(h);
   if (flags & MI_HGEMM_TUNE_PERSIST) {
     if (h->table_path.empty()) return MI_HGEMM_ERR_IO;
     FILE* f = std::fopen(h->table_path.c_str(), "a");
