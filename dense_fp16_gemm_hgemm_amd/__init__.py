@@ -30,7 +30,7 @@ __all__ = [
     "mi_hgemm_create", "mi_hgemm_create_ex", "mi_hgemm_destroy", "mi_hgemm_run",
     "mi_hgemm_run_kernel", "mi_hgemm_plan", "mi_hgemm_tune", "mi_hgemm_status_string",
     "mi_hgemm_last_hip_error", "mi_hgemm_kernel_count", "mi_hgemm_kernel_name",
-    "mi_hgemm_table_size", "mi_hgemm_table_save",
+    "mi_hgemm_table_size", "mi_hgemm_table_save", "mi_hgemm_run_noalloc",
 ]
 
 MI_HGEMM_OK = 0
@@ -72,6 +72,8 @@ _run_kernel = _sig("mi_hgemm_run_kernel", ctypes.c_int, _p, _i32, _i32, _i32, _i
                    _i64, _p, _i64, _p, _i64, _p, _i64, ctypes.c_int, _p)
 _plan = _sig("mi_hgemm_plan", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
              ctypes.c_int, _I32P, _I32P, _I32P, _I32P)
+_run_noalloc = _sig("mi_hgemm_run_noalloc", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p,
+                    _i64, _p, _i64, ctypes.c_int, _p)
 _run_i8 = _sig("mi_hgemm_run_i8", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
                _i64, ctypes.c_int, _p)
 _plan_i8 = _sig("mi_hgemm_plan_i8", ctypes.c_int, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
@@ -111,6 +113,11 @@ def mi_hgemm_destroy(h):
 
 def mi_hgemm_run(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN, stream=None):
     return _run(h, M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
+
+
+def mi_hgemm_run_noalloc(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN,
+                         stream=None):
+    return _run_noalloc(h, M, N, K, A, lda, B, ldb, C, ldc, layout, stream)
 
 
 def mi_hgemm_run_i8(h, M, N, K, A, lda, B, ldb, C, ldc, layout=MI_HGEMM_LAYOUT_TN, stream=None):

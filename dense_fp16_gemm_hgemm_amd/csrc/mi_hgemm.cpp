@@ -114,7 +114,73 @@ struct mi_hgemm_ctx {
   std::mutex memo_mu;      // guards memo (run/plan may be called from several threads)
 };
 
+// ------------------------------------------------------ static scratch --
+// The split-K scratch of mi_hgemm_run_noalloc: partial tiles, then one arrival
+// counter per output tile.  Each device that loads the library holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its address on a device is resolved once per
+// device (static_scratch_init) and only that address is ever used.
 namespace {
+constexpr size_t kStaticPartialBytes = size_t(MI_HGEMM_NOALLOC_PARTIAL_BYTES);
+constexpr int64_t kStaticCounters = MI_HGEMM_NOALLOC_TILE_COUNTERS;
+constexpr size_t kStaticBytes = kStaticPartialBytes + size_t(kStaticCounters) * sizeof(int);
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+namespace {
+
+struct StaticScratch {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};      // device address of `scratch` per device, once resolved
+  hipError_t err[kMaxDevices] = {};  // why resolving failed, if it did
+};
+StaticScratch& static_scratch() {
+  static StaticScratch s;
+  return s;
+}
+
+// With device `dev` current: resolve the array's address on it and clear its
+// counters (they must start at zero; every split launch leaves them at zero).
+// Runs once per device, at handle creation (no stream is being captured then).
+void static_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  StaticScratch& st = static_scratch();
+  std::lock_guard<std::mutex> lk(st.mu);
+  if (st.ptr[dev]) return;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && ptr == nullptr) e = hipErrorInvalidSymbol;
+  if (e == hipSuccess)
+    e = hipMemset(static_cast<char*>(ptr) + kStaticPartialBytes, 0, kStaticCounters * sizeof(int));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    st.err[dev] = e;
+    return;
+  }
+  st.ptr[dev] = ptr;
+  st.err[dev] = hipSuccess;
+}
+
+// The resolved scratch of device `dev` as a workspace (ws == nullptr if it
+// could not be resolved; *err then says why).
+Workspace static_ws(int dev, hipError_t* err) {
+  Workspace w;
+  *err = hipErrorInvalidDevice;
+  if (dev < 0 || dev >= kMaxDevices) return w;
+  StaticScratch& st = static_scratch();
+  std::lock_guard<std::mutex> lk(st.mu);
+  *err = st.ptr[dev] ? hipSuccess : (st.err[dev] != hipSuccess ? st.err[dev] : hipErrorNotInitialized);
+  if (!st.ptr[dev]) return w;
+  char* base = static_cast<char*>(st.ptr[dev]);
+  w.ws = reinterpret_cast<float*>(base);
+  w.cnt = reinterpret_cast<int*>(base + kStaticPartialBytes);
+  w.ws_bytes = kStaticPartialBytes;
+  w.max_tiles = kStaticCounters;
+  return w;
+}
 
 bool is_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -574,6 +640,8 @@ mi_hgemm_status_t mi_hgemm_create_ex(mi_hgemm_handle_t* out, const char* table_p
       if (cnt) (void)hipFree(cnt);
       (void)hipGetLastError();
     }
+    // the no-allocation entry point's scratch on this device (once per device)
+    static_scratch_init(h->device);
   }
   bool named = false;
   if (table_path && *table_path) {
@@ -650,6 +718,36 @@ mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int
                                   const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                                   int64_t ldc, mi_hgemm_layout_t layout, void* stream) {
   return run_impl(h, mihg::DTYPE_I8, M, N, K, A, lda, B, ldb, C, ldc, layout, stream);
+}
+
+mi_hgemm_status_t mi_hgemm_run_noalloc(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                                       void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                       void* stream) {
+  if (!h) return MI_HGEMM_ERR_INVALID_ARG;
+  const mi_hgemm_status_t st = validate(mihg::DTYPE_F16, M, N, K, A, lda, B, ldb, C, ldc, layout);
+  if (st != MI_HGEMM_OK) return st;
+  if (M == 0 || N == 0) return MI_HGEMM_OK;
+  if (h->no_device) return MI_HGEMM_ERR_NO_DEVICE;
+  hipError_t err = hipSuccess;
+  const Workspace w = static_ws(h->device, &err);
+  if (!w.ws) return hip_fail(h, err);
+  Config c;
+  c.kernel = kGenericKernel;
+  if (K > 0) {
+    c = select(h, M, N, K, make_cls(mihg::DTYPE_F16, aligned_class(mihg::DTYPE_F16, K, A, lda, B, ldb, C, ldc)),
+               false);
+    // The array holds fewer partial tiles than a handle's workspace: a planned
+    // split that does not fit is halved until it does (split 1 needs none).
+    // launch() still refuses any split beyond the array (UNSUPPORTED).
+    while (c.splitk > 1) {
+      int64_t chunk = K;
+      if (effective_split(kKernels[c.kernel], M, N, K, c.splitk, &chunk, w.ws_bytes, w.max_tiles) >= 1)
+        break;
+      c.splitk /= 2;
+    }
+  }
+  return run_config(h, mihg::DTYPE_F16, c, M, N, K, A, lda, B, ldb, C, ldc, stream, w);
 }
 
 mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index, int32_t group_m,

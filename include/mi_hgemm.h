@@ -213,6 +213,36 @@ mi_hgemm_status_t mi_hgemm_run_kernel(mi_hgemm_handle_t h, int32_t kernel_index,
                                       void* C, int64_t ldc, mi_hgemm_layout_t layout,
                                       void* stream);
 
+/*
+ * mi_hgemm_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, validation, dispatch, alignment rules and return codes are those
+ * of mi_hgemm_run, and the call allocates nothing (device or host).  The one
+ * difference is where a split-K launch keeps its fp32 partial tiles and its
+ * per-tile arrival counters: not in the handle's workspace but in a static
+ * device array of the library, MI_HGEMM_NOALLOC_PARTIAL_BYTES of partials and
+ * MI_HGEMM_NOALLOC_TILE_COUNTERS counters.  Each device holds its own copy of
+ * the array until the process ends; its address is resolved and its counters
+ * cleared when the first handle is created on that device (ERR_HIP here if
+ * that failed; mi_hgemm_last_hip_error says why).
+ *   - A planned K split whose partial tiles do not fit the array is halved
+ *     until they do (split 1 needs no scratch), so no shape is refused for
+ *     lack of scratch, and no launch is issued with more partials or counters
+ *     than the array holds (UNSUPPORTED if one would be).  With a different
+ *     split the sum is the same; for non-integer operands its rounding may
+ *     differ from mi_hgemm_run's within the tolerance of the operation.
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's partials; the counters are back at zero after every launch.
+ *     Calls on one device that may overlap in time (different streams, or
+ *     threads without ordering) race on the array: order them on one stream.
+ */
+#define MI_HGEMM_NOALLOC_PARTIAL_BYTES (16u << 20)
+#define MI_HGEMM_NOALLOC_TILE_COUNTERS 4096
+mi_hgemm_status_t mi_hgemm_run_noalloc(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                                       void* C, int64_t ldc, mi_hgemm_layout_t layout,
+                                       void* stream);
+
 /* Number of (shape -> config) entries the handle holds. */
 int mi_hgemm_table_size(mi_hgemm_handle_t h);
 
