@@ -14,7 +14,6 @@ import pytest
 import torch
 
 import oracle
-from parity import sample_indices
 
 pytestmark = pytest.mark.gpu
 
@@ -132,18 +131,19 @@ def test_i8_llm_shapes_dispatch(lib, p):
     A, Bt = inputs.make(p)
     log(f"{p.name} plan {lib.plan(gpu(A[:1]), gpu(Bt[:1]))}")
     got = host(lib.run_i8(gpu(A), gpu(Bt)))
-    r, c = sample_indices(p.M, p.N, 3000, seed=p.seed)
-    check_exact(got[r, c], oracle.igemm_tn_entries(A, Bt, r, c), p.name)
+    check_exact(got, oracle.igemm_tn(A, Bt), p.name)
 
 
-def test_i8_square_8192_sampled(lib):
+@pytest.mark.slow
+def test_i8_square_8192_every_element(lib):
+    """The int8 8192^3 problem the benchmark times, every element exact."""
     p = inputs.i8_square()
     A, Bt = inputs.make(p)
     dA, dB = gpu(A), gpu(Bt)
     log(f"{p.name} plan {lib.plan(dA, dB)}")
     got = host(lib.run_i8(dA, dB))
-    r, c = sample_indices(p.M, p.N, 4000, seed=11)
-    check_exact(got[r, c], oracle.igemm_tn_entries(A, Bt, r, c), p.name)
+    del dA, dB
+    check_exact(got, oracle.igemm_tn(A, Bt), p.name)
 
 
 def test_i8_misaligned_operands_take_the_elementwise_instance(lib):

@@ -2,8 +2,9 @@
 
 Every case draws seeded inputs from dense_fp16_gemm_hgemm_amd.inputs, runs the
 GPU library, copies C back and compares with the oracle (tests/parity.py for
-the rules).  Sizes the oracle finishes in seconds are compared element by
-element; the full benchmark sizes are compared on sampled elements.
+the rules), element by element.  The full benchmark sizes are compared in full
+in tests/test_gpu_full_size.py; the sampled variants here (8192^3 and the
+M >= 256 projection shapes on a few thousand entries) are the quick form.
 """
 import sys
 
@@ -176,9 +177,9 @@ def test_integer_variant_bitexact_every_config_shape(lib, shape):
     A, Bt = rand_problem(M, N, K, "int", seed=3 + M + N + K)
     log(f"int {M}x{N}x{K}")
     got = host(lib.run(gpu(A), gpu(Bt)))
-    if M * N * K <= 64 * 4096 * 4096:
+    if M * N * K < 8192 ** 3:
         check_bitexact(got, oracle.hgemm_tn(A, Bt), f"int {shape}")
-    else:
+    else:   # every element of 8192^3 in tests/test_gpu_full_size.py
         r, c = sample_indices(M, N, 4096, seed=M)
         check_bitexact(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), f"int {shape}")
 
@@ -255,6 +256,78 @@ def test_subnormal_inputs(lib):
     assert np.count_nonzero(np.abs(A) < 2.0 ** -14) > 1000
     got = host(lib.run(gpu(A), gpu(Bt)))
     check_tolerance(got, oracle.hgemm_tn(A, Bt), "subnormal inputs")
+
+
+def _all_subnormal_bt(N, K):
+    """Bt (N x K) holding every nonzero binary16 subnormal pattern -- 0x0001..0x03FF
+    and 0x8001..0x83FF, 2046 of them -- once forwards and once backwards, zeros
+    after that."""
+    pats = np.concatenate([np.arange(0x0001, 0x0400), np.arange(0x8001, 0x8400)]).astype(np.uint16)
+    assert N * K >= 2 * pats.size
+    flat = np.zeros(N * K, np.uint16)
+    flat[:pats.size] = pats
+    flat[pats.size:2 * pats.size] = pats[::-1]
+    return flat.reshape(N, K).view(np.float16)
+
+
+@pytest.mark.parametrize("kidx", F16_KIDX, ids=[mh.kernel_names()[i] for i in F16_KIDX])
+def test_subnormals_bitexact_every_instance(lib, kidx):
+    """Whether the matrix cores keep binary16 subnormals, answered bit for bit.
+
+    (a) A = I: C = B, so every subnormal input must come out unchanged
+        (subnormal in, subnormal out: a flush of either shows as 0);
+    (b) A = 1024 I: C = 1024 B, normal results of subnormal inputs (a flush of
+        the inputs shows as 0);
+    (c) normal inputs whose sums are subnormal: A, B = U{-4..4} * 2^-12 with
+        K = 56, so every partial sum is a multiple of 2^-24 below 1024 * 2^-24
+        in magnitude, exact in fp32 and in binary16 (a flush of the fp32 ->
+        binary16 conversion shows as 0).
+    Every product and sum is exact, so the oracle's single rounding and the
+    GPU's must agree bit for bit."""
+    name = mh.kernel_names()[kidx]
+    K = 64
+    Bt = _all_subnormal_bt(64, K)
+    cases = []
+    for scale in (1.0, 1024.0):
+        A = (np.eye(K) * scale).astype(np.float16)
+        cases.append((f"A={scale:g}*I", A, Bt))
+    rng = np.random.default_rng(77)
+    A3 = (rng.integers(-4, 5, (64, 56)) * 2.0 ** -12).astype(np.float16)
+    B3 = (rng.integers(-4, 5, (72, 56)) * 2.0 ** -12).astype(np.float16)
+    cases.append(("subnormal sums", A3, B3))
+    for what, A, B in cases:
+        log(f"subnormal {name} {what}")
+        ref = oracle.hgemm_tn(A, B)
+        if what == "A=1*I":
+            assert np.array_equal(ref.view(np.uint16), B.T.view(np.uint16))
+        if what == "subnormal sums":
+            assert np.count_nonzero(np.abs(ref) < 2.0 ** -14) > ref.size // 2
+        got = host(lib.run_kernel(kidx, gpu(A), gpu(B), padded_out(A.shape[0], B.shape[0])))
+        check_bitexact(got, ref, f"{name} {what}")
+
+
+STAGED_C = [n for n in mh.kernel_names() if n.endswith("_sc") or n.startswith("d2tile3p_")]
+
+
+@pytest.mark.parametrize("kernel", STAGED_C)
+@pytest.mark.parametrize("K", [64, 200], ids=["K64_nt_stores", "K200_cached_stores"])
+def test_staged_c_leaves_padding_untouched(lib, kernel, K):
+    """The instances that stage C through LDS (and the persistent grid) write
+    whole 16-byte row chunks.  With N a multiple of 8, ldc = N + 8 and a ragged
+    M, every element outside the M x N block -- the padding columns [N, ldc) of
+    each row and the rows after M -- keeps its sentinel value.  K <= 128 takes
+    the non-temporal stores, K > 128 the cached ones."""
+    M, N = 300, 520
+    ldc = N + 8
+    A, Bt = rand_problem(M, N, K, "int", seed=K + M)
+    buf = torch.full((M + 3, ldc), 7.0, dtype=torch.float16, device=DEV)
+    out = buf[:M, :N]
+    log(f"staged C padding {kernel} {M}x{N}x{K} ldc={ldc}")
+    lib.run_kernel(kernel, gpu(A), gpu(Bt), out, group_m=4, xcd_remap=1)
+    full = host(buf)
+    check_bitexact(full[:M, :N], oracle.hgemm_tn(A, Bt), f"{kernel} K={K}")
+    assert np.all(full[:M, N:] == np.float16(7.0)), "padding columns were written"
+    assert np.all(full[M:] == np.float16(7.0)), "rows past M were written"
 
 
 def test_overflow_to_infinity(lib):
@@ -405,13 +478,12 @@ def _sweep_sample():
 @pytest.mark.parametrize("p", _sweep_sample(), ids=lambda p: p.name)
 def test_shape_sweep_sample(lib, p):
     """Sweep problems through the dispatcher (table, nearest entry or heuristic,
-    whichever the shape reaches): sampled entries within tolerance."""
+    whichever the shape reaches): every element within tolerance."""
     A, Bt = inputs.make(p)
     dA, dB = gpu(A), gpu(Bt)
     log(f"sweep {p.name}: {lib.plan(dA, dB)}")
     got = host(lib.run(dA, dB))
-    r, c = sample_indices(p.M, p.N, 2048, seed=p.seed)
-    check_tolerance(got[r, c], oracle.hgemm_tn_entries(A, Bt, r, c), p.name)
+    check_tolerance(got, oracle.hgemm_tn(A, Bt), p.name)
 
 
 @pytest.mark.parametrize("M,N", [(128, 256), (64, 64)])
