@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "ring_schedule.h"
 
 namespace mihg {
 
@@ -892,7 +893,9 @@ __device__ inline int ntiles_of(int tiles_m, int tiles_n) { return tiles_m * til
 // halves, one 16-row slice at a time, and are stored as 16-byte row chunks
 // (whole row segments of the wave's columns) instead of 8-byte pieces of 16
 // rows.  The scratch's 16-byte chunks are XORed with the row's low bits.  One
-// wave's LDS writes and reads complete in order, so a slice needs no barrier.
+// wave's LDS writes and reads complete in order, so a slice needs no
+// workgroup barrier; wave barriers between its write and read phases keep the
+// compiler from reordering them.
 // row0: the wave's first row within the tile; col0: its first column of C;
 // rsc covers the tile's rows; columns at or past N are dropped (N % 8 == 0).
 // (d2tile_body inlines the same steps: through this helper its 4-wave 256x256
@@ -916,6 +919,9 @@ __device__ __forceinline__ void store_c_staged(const Acc (&acc)[FM][FN], _Float1
       const int ch = (col >> 3) ^ (srow & SWM);
       *reinterpret_cast<h4*>(scr + srow * WTN + ch * 8 + (col & 7)) = o;
     }
+    // the slice's writes stay before its reads, and (below) its reads before
+    // the next slice's writes, whatever the compiler proves about aliasing
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int q = 0; q < 16 * CPRW / 64; ++q) {
       const int idx = q * 64 + lane, r = idx / CPRW, c = idx % CPRW;
@@ -925,6 +931,7 @@ __device__ __forceinline__ void store_c_staged(const Acc (&acc)[FM][FN], _Float1
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc,
                                              j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, 0, 0);
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1005,7 +1012,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
           lds0 + (uint32_t)((B_OFF + bst * B_STRIDE + blk * 8 * kD2Row) * 2));
   };
   auto dma_one = [&](int ast, int bst, int ka, int kb, int x) {
-    if constexpr (SA == 2) {
+    if constexpr (!ring::d2_b_first(SA)) {
       if (x < A_BLK) dma_a(ast, ka, x);
       else dma_b(bst, kb, x - A_BLK);
     } else {
@@ -1084,9 +1091,11 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto wait_all = [&]() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8)); };  // vmcnt(0)
-  // vmcnt(A_BLK): all but this wave's last A_BLK copies have landed
-  auto wait_but_a = [&]() {
-    constexpr int n = A_BLK;
+  // at a trip's end (and after the prologue) all but this wave's last
+  // ring::d2_in_flight copies have landed: with three A stages the A copies
+  // of the tile two ahead may still fly
+  auto wait_in_flight = [&]() {
+    constexpr int n = ring::d2_in_flight(SA, A_BLK);
     static_assert(n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   };
@@ -1110,8 +1119,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
   // across it; an empty asm makes the wave index opaque to that hoisting.
   if constexpr (PERSIST) asm volatile("" : "+s"(wave_u));
   if (first) {
-    if constexpr (SA == 3) wait_but_a();
-    else wait_all();
+    wait_in_flight();
   } else {
     wait_all();  // the previous tile's C stores count in vmcnt too
   }
@@ -1134,16 +1142,14 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     for (int fn = 0; fn < FN; ++fn) fb[1][u][fn] = zero_h8();
   }
   for (int kt = 0; kt < nk; ++kt) {
-    // tile kt is in A stage kt % SA and B stage kt % 2; this trip copies B of
+    // tile kt is in A stage tr.ra and B stage tr.rb; this trip copies B of
     // tile kt+1 and A of tile kt+SA-1 into the stages tile kt-1 left
-    const int ast = SA == 2 ? (kt & 1) : kt % 3, bst = kt & 1;
-    const int wast = SA == 2 ? (ast ^ 1) : (ast == 0 ? 2 : ast - 1);
+    const ring::Trip tr = ring::d2_trip(kt, SA);
     // first half: step 1 of tile kt-1, the copies, step-0 fragments of tile kt
-    half(T{}, T{}, I1{}, I0{}, ast, bst, (kt + SA - 1) * BK, (kt + 1) * BK, wast, bst ^ 1);
+    half(T{}, T{}, I1{}, I0{}, tr.ra, tr.rb, tr.ta * BK, tr.tb * BK, tr.wa, tr.wb);
     // second half: step 0 of tile kt, step-1 fragments of tile kt
-    half(T{}, F{}, I0{}, I1{}, ast, bst, 0, 0, 0, 0);
-    if constexpr (SA == 3) wait_but_a();  // tile kt+1 has landed; A of kt+2 may fly
-    else wait_all();
+    half(T{}, F{}, I0{}, I1{}, tr.ra, tr.rb, 0, 0, 0, 0);
+    wait_in_flight();  // tile kt+1 has landed; with SA = 3 A of kt+2 may fly
     __syncthreads();
   }
   // this output tile's origin (m0, n0 move on to the next tile below)
@@ -1171,7 +1177,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[1][u][fn], fa[1][u][fm], acc[fm][fn]);
-  if constexpr (SA == 3) {
+  if constexpr (ring::d2_in_flight(SA, A_BLK) > 0) {
     if (!more) wait_all();  // A copies past the last tile drain before exit
   }
 
@@ -1212,7 +1218,9 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
           *reinterpret_cast<h4*>(scr + srow * WTN + ch * 8 + (col & 7)) = o;
         }
         // one wave's LDS writes and reads complete in order: the reads below
-        // see the writes above, and the next fm's writes follow these reads
+        // see the writes above, and the next fm's writes follow these reads;
+        // the wave barriers keep the compiler from moving either across
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int q = 0; q < 16 / RPI; ++q) {
           const int r = q * RPI + lane / CPRW, c = lane % CPRW;
@@ -1225,6 +1233,7 @@ __device__ __forceinline__ void d2tile_body(const GemmArgs& p) {
           else
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc, off, 0, 0);
         }
+        __builtin_amdgcn_wave_barrier();
       }
     }
   }
@@ -1601,7 +1610,7 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
   };
   // copy x of a trip: A's then B's (SB = S), or B's then A's (SB = S - 1)
   auto dma_one = [&](int ast, int bst, int ka, int kb, int x) {
-    if constexpr (SB == S) {
+    if constexpr (!ring::k_b_first(S, SB)) {
       if (x < A_BLK) dma_a(ast, ka, x);
       else dma_b(bst, kb, x - A_BLK);
     } else {
@@ -1673,7 +1682,7 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
   };
   // at a trip's end the copies issued after the next tile's may stay in flight
-  using WaitInFlight = std::integral_constant<int, A_BLK * (S - 2) + B_BLK * (SB - 2)>;
+  using WaitInFlight = std::integral_constant<int, ring::k_in_flight(S, SB, A_BLK, B_BLK)>;
   using WaitAll = std::integral_constant<int, 0>;
 
   const int nk = (k_end - k_begin + BK - 1) / BK;
@@ -1695,10 +1704,10 @@ __device__ __forceinline__ void ktile_body(const GemmArgs& p) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) fb[1][fn] = zero_h8();
   for (int kt = 0; kt < nk; ++kt) {
-    const int ast = kt % S, wast = (kt + S - 1) % S;
-    const int bst = SB == S ? ast : kt % SB, wbst = SB == S ? wast : (kt + SB - 1) % SB;
-    const int ka = k_begin + (kt + S - 1) * BK, kb = k_begin + (kt + SB - 1) * BK;
-    part(std::integral_constant<int, 0>{}, ast, bst, ka, kb, wast, wbst);
+    const ring::Trip tr = ring::k_trip(kt, S, SB);
+    const int ast = tr.ra, bst = tr.rb;
+    const int ka = k_begin + tr.ta * BK, kb = k_begin + tr.tb * BK;
+    part(std::integral_constant<int, 0>{}, ast, bst, ka, kb, tr.wa, tr.wb);
     part(std::integral_constant<int, 1>{}, ast, bst, 0, 0, 0, 0);
     part(std::integral_constant<int, 2>{}, ast, bst, 0, 0, 0, 0);
     part(std::integral_constant<int, 3>{}, ast, bst, 0, 0, 0, 0);
