@@ -6,7 +6,9 @@ linked into ``dense_fp16_gemm_hgemm_amd/libmi_hgemm.so``.  Packed fp32 VALU
 instructions are disabled for all device code.
 
 It also builds ``dense_fp16_gemm_hgemm_amd/libmi_overlap.so`` (the load/compute
-overlap micro-benchmark, ``overlap/overlap.hip``) and, where rocBLAS is
+overlap micro-benchmark, ``overlap/overlap.hip``),
+``dense_fp16_gemm_hgemm_amd/libmi_ceiling.so`` (the MFMA, copy and HBM read
+ceilings, ``ceiling/ceiling.hip``) and, where rocBLAS is
 installed, ``dense_fp16_gemm_hgemm_amd/mi_hgemm_serve``, the server-mode load
 generator (``serve/serve_bench.cpp``), linked against the library (found beside
 it at run time) and rocBLAS (the vendor backend it compares with).  Without
@@ -30,6 +32,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libmi_hgemm.so")
 OVERLAP_SRC = os.path.join(PKG, "overlap", "overlap.hip")
 OVERLAP_PATH = os.path.join(PKG, "libmi_overlap.so")
+CEILING_SRC = os.path.join(PKG, "ceiling", "ceiling.hip")
+CEILING_PATH = os.path.join(PKG, "libmi_ceiling.so")
 SERVE_SRC = os.path.join(PKG, "serve", "serve_bench.cpp")
 SERVE_PATH = os.path.join(PKG, "mi_hgemm_serve")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -94,6 +98,15 @@ def build(verbose: bool = False) -> str:
         print(r.stdout.decode(errors="replace"), file=sys.stderr)
         raise RuntimeError("hipcc failed for " + OVERLAP_SRC)
     os.replace(tmp, OVERLAP_PATH)
+    # the MFMA probe's chains stay in their registers (no accumulator copies
+    # between rounds) only with the VGPR form of the MFMA
+    tmp = CEILING_PATH + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, *COMMON, *DEVICE, "-mllvm", "-amdgpu-mfma-vgpr-form", "-shared",
+                        CEILING_SRC, "-o", tmp], stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        print(r.stdout.decode(errors="replace"), file=sys.stderr)
+        raise RuntimeError("hipcc failed for " + CEILING_SRC)
+    os.replace(tmp, CEILING_PATH)
     if not (os.path.exists(ROCBLAS_HEADER) and glob.glob(ROCBLAS_LIB)):
         print(f"note: rocBLAS not found ({ROCBLAS_HEADER}); the server-mode load generator "
               "(which compares with it) is not built", file=sys.stderr)
