@@ -64,6 +64,17 @@ namespace mihg {
 #define MIHG_PPTILE_INSTANCES(X) \
   X(256, 256)                    \
   X(256, 128)
+// PP2TILE: X(BM, BN): two groups taking turns, one whole K tile per turn;
+// PP2TILESC: the same with C staged through LDS (wave tiles of 32 or 64 columns)
+#define MIHG_PP2TILE_INSTANCES(X) \
+  X(256, 256)                     \
+  X(256, 192)                     \
+  X(256, 128)                     \
+  X(128, 256)
+#define MIHG_PP2TILESC_INSTANCES(X) \
+  X(256, 256)                       \
+  X(256, 128)                       \
+  X(128, 256)
 
 // Int8 variant (int8 operands, int32 results).  I8_D2TILE: X(BM, BN, WGM, WGN),
 // K step 128; I8_KTILE: X(BM, BN, WGM, WGN, BK, S), K step BK of 256 or 512.
@@ -90,6 +101,8 @@ namespace mihg {
 // tiles that serve outputs of at most 64 rows, where B is streamed once
 #define MIHG_KTILE_NT_INSTANCES(X) \
   X(64, 64, 2, 2, 128, 3)          \
+  X(64, 64, 2, 4, 128, 3)          \
+  X(32, 64, 2, 4, 128, 3)          \
   X(64, 128, 2, 2, 128, 3)         \
   X(32, 64, 2, 2, 128, 3)          \
   X(16, 64, 1, 4, 256, 3)          \
@@ -118,11 +131,21 @@ namespace mihg {
 #define MIHG_D2TILE3SC_INSTANCES(X) \
   X(256, 256, 2, 4)                 \
   X(256, 256, 2, 2)
+// (8-wave forms of the small tiles: a CU's global -> LDS copy rate rises
+// with the number of waves issuing copies, ~54 GB/s with 4 and ~64 GB/s with
+// 8 on L2-resident data, and these tiles are bound by that rate; the
+// two-stage 64 x 64 forms fit two workgroups in a CU's LDS.  The staged C
+// store needs wave tiles at least 32 columns wide.)
 #define MIHG_KTILESC_INSTANCES(X) \
   X(128, 128, 2, 4, 128, 3, 2)     \
   X(128, 128, 2, 2, 128, 3, 2)     \
   X(64, 64, 2, 2, 128, 3, 3)       \
-  X(32, 64, 2, 2, 128, 3, 3)
+  X(32, 64, 2, 2, 128, 3, 3)       \
+  X(64, 64, 4, 2, 128, 3, 3)       \
+  X(128, 64, 4, 2, 128, 3, 3)      \
+  X(64, 128, 2, 4, 128, 3, 3)      \
+  X(64, 64, 2, 2, 128, 2, 2)       \
+  X(64, 64, 4, 2, 128, 2, 2)
 #define MIHG_D2TILESC_INSTANCES(X) \
   X(128, 128, 2, 2)
 #define MIHG_KTILE_NS_B_INSTANCES(X) \
@@ -181,6 +204,8 @@ namespace mihg {
 #define INSTANTIATE_I8_D2TILE3(BM, BN, WGM, WGN) \
   template __global__ void i8_d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
+#define INSTANTIATE_PP2TILE(BM, BN) template __global__ void pp2tile_kernel<BM, BN, 16>(GemmArgs);
+#define INSTANTIATE_PP2TILESC(BM, BN) template __global__ void pp2tilesc_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S, S>(GemmArgs);
 #define INSTANTIATE_KTILE_B(BM, BN, WGM, WGN, BK, S, SB) \
@@ -215,6 +240,8 @@ MIHG_DTILE_INSTANCES(INSTANTIATE_DTILE)
 MIHG_D2TILE_INSTANCES(INSTANTIATE_D2TILE)
 MIHG_D2TILE3_INSTANCES(INSTANTIATE_D2TILE3)
 MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
+MIHG_PP2TILE_INSTANCES(INSTANTIATE_PP2TILE)
+MIHG_PP2TILESC_INSTANCES(INSTANTIATE_PP2TILESC)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
 MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
@@ -256,6 +283,12 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
 #define PPTILE_DESC(BM, BN)                                                                \
   {"pptile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                     \
    2 * (BM + BN) * kD2Row * 2, 0, &launch_pptile<BM, BN>, &grid_tile<BM, BN>},
+#define PP2TILE_DESC(BM, BN)                                                               \
+  {"pp2tile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                    \
+   (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_pp2tile<BM, BN, 16>, &grid_tile<BM, BN>},
+#define PP2TILESC_DESC(BM, BN)                                                             \
+  {"pp2tile_" #BM "x" #BN "_w8_m16_sc", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                 \
+   (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_pp2tilesc<BM, BN>, &grid_tile<BM, BN>},
 #define KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1,                                             \
@@ -320,6 +353,8 @@ const KernelDesc kKernels[] = {
     MIHG_D2TILE_INSTANCES(D2TILE_DESC)
     MIHG_D2TILE3_INSTANCES(D2TILE3_DESC)
     MIHG_PPTILE_INSTANCES(PPTILE_DESC)
+    MIHG_PP2TILE_INSTANCES(PP2TILE_DESC)
+    MIHG_PP2TILESC_INSTANCES(PP2TILESC_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_KTILE_B_INSTANCES(KTILE_B_DESC)
     MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)

@@ -900,10 +900,12 @@ __device__ inline int ntiles_of(int tiles_m, int tiles_n) { return tiles_m * til
 // rsc covers the tile's rows; columns at or past N are dropped (N % 8 == 0).
 // (d2tile_body inlines the same steps: through this helper its 4-wave 256x256
 // form, which uses every register, spilled one value.)
+// nt: store with the non-temporal policy (short K: the launch is mostly C
+// traffic, which then streams past the caches instead of evicting its own lines).
 template <int FM, int FN, int WTN, typename Acc>
 __device__ __forceinline__ void store_c_staged(const Acc (&acc)[FM][FN], _Float16* scr,
                                                __amdgpu_buffer_rsrc_t rsc, int row0, int col0,
-                                               int N, int64_t ldc, int lane) {
+                                               int N, int64_t ldc, int lane, bool nt = false) {
   constexpr int CPRW = WTN / 8;                  // 16-byte chunks per scratch row
   constexpr int SWM = CPRW >= 8 ? 7 : CPRW - 1;  // XOR mask of the chunk index
   static_assert(CPRW % 4 == 0 && (CPRW & (CPRW - 1)) == 0, "power-of-two rows of >= 4 chunks");
@@ -928,8 +930,11 @@ __device__ __forceinline__ void store_c_staged(const Acc (&acc)[FM][FN], _Float1
       const h8 x = *reinterpret_cast<const h8*>(scr + r * WTN + ((c ^ (r & SWM)) * 8));
       const int i = row0 + fm * 16 + r;
       const int j = col0 + c * 8;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc,
-                                             j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, 0, 0);
+      const uint32_t off = j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB;
+      if (nt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc, off, 0, 2);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsc, off, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -1504,6 +1509,244 @@ pptile_kernel(GemmArgs p) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Full-tile ping-pong family ("pp2tile"): BM x BN x 64 tiles, 8 waves in two
+// groups of four; every SIMD holds one wave of each group.  Time is cut into
+// phases by workgroup barriers.  In each phase one group multiplies a whole K
+// tile -- all 2 x FM x FN MFMAs back to back from fragments already in its
+// registers, at raised wave priority -- while the other group reads its
+// fragments of its next K tile from LDS and issues copies, so each SIMD's
+// matrix pipe is fed by one wave that never waits on memory.  ([P1] 正文
+// paragraph 3 and 可落地参数清单: producer and consumer warp groups that take
+// turns, here without a dedicated producer: each group is both in turn.)
+//
+// Group 0 owns output rows [0, BM/2), group 1 rows [BM/2, BM); wave w4 of a
+// group owns columns [w4 * BN/4, (w4 + 1) * BN/4).  K tile kt is multiplied by
+// group 0 in phase 2kt and by group 1 in phase 2kt+1, whose fragments the
+// group read in its phase before.  LDS: d2tile3's ring (three A stages, two
+// B stages, 128-byte rows, chunk XOR (row >> 1) & 7); A and B are both copied
+// two tiles ahead, A by group 1 (in its memory phase 2kt, before its reads)
+// and B by group 0 (in phase 2kt+1); ring::pp_trip gives the stages.  Group 1
+// ends each memory phase with its previous A tile landed, group 0 each
+// compute phase with its previous B tile landed, so tile kt+1 is complete
+// before the barrier that opens its first reads (phase 2kt+1).
+template <int BM, int BN, bool SC, int MF = 16>
+__device__ __forceinline__ void pp2_body(const GemmArgs& p) {
+  using MM = Mfma<MF>;
+  constexpr int BK = 64, KSTEPS = BK / MM::KI, CPS = MM::KI / 8;  // CPS: 16-byte chunks per k-step
+  static_assert(!SC || MF == 16, "the staged C store takes 16 x 16 blocks");
+  constexpr int WTM = BM / 2, WTN = BN / 4;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int A_BLK = BM / 8 / 4, B_BLK = BN / 8 / 4;  // 1 KiB copies per wave of the copying group
+  constexpr int A_STRIDE = BM * kD2Row, B_OFF = 3 * BM * kD2Row, B_STRIDE = BN * kD2Row;
+  constexpr int LDS_HALVES = 3 * BM * kD2Row + 2 * BN * kD2Row;
+  static_assert(LDS_HALVES * 2 <= 160 * 1024, "LDS budget");
+  static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must hold whole MFMA blocks");
+  static_assert(A_BLK % 2 == 0 && B_BLK % 2 == 0, "copy blocks pair up by parity");
+
+  __shared__ __attribute__((aligned(1024))) _Float16 lds[LDS_HALVES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
+
+  // copies: lane l -> row l/8 of an 8-row block, physical chunk l%8, which
+  // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
+  const int drow = lane >> 3;
+  const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
+                             (uint32_t)(min(BM, M - m0) * lda * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
+                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const int64_t ldx = grp == 1 ? lda : ldb;
+  const uint32_t v0 = (uint32_t)(drow * ldx * 2 + dch0 * 16), v1 = (uint32_t)(drow * ldx * 2 + dch1 * 16);
+  const bool mask_k = (K & 63) != 0;
+  const uint32_t lds0 = lds_addr(lds);
+  // this wave's copies of K tile t: group 1 copies its quarter of A's rows into
+  // A stage `st` (copy_a), group 0 its quarter of B's rows into B stage `st`
+  // (copy_b); chunks at or past K read 0
+  auto copy_a = [&](int st, int t) {
+    const uint32_t kb = (uint32_t)(t * BK) * 2;
+#pragma unroll
+    for (int x = 0; x < A_BLK; ++x) {
+      const int ch = (x & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (t * BK + ch * 8 < K);
+      const int blk = w4 * A_BLK + x;
+      dma16(rda, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
+            lds0 + (uint32_t)((st * A_STRIDE + blk * 8 * kD2Row) * 2));
+    }
+  };
+  auto copy_b = [&](int st, int t) {
+    const uint32_t kb = (uint32_t)(t * BK) * 2;
+#pragma unroll
+    for (int x = 0; x < B_BLK; ++x) {
+      const int ch = (x & 1) ? dch1 : dch0;
+      const bool kin = !mask_k || (t * BK + ch * 8 < K);
+      const int blk = w4 * B_BLK + x;
+      dma16(rdb, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
+            lds0 + (uint32_t)((B_OFF + st * B_STRIDE + blk * 8 * kD2Row) * 2));
+    }
+  };
+
+  // fragments of k-step s: the lane's row at logical chunk 4s + l/16
+  const int frow = lane % MF, fq = lane / MF, fsw = (frow >> 1) & 7;
+  int fa_off[KSTEPS], fb_off[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int phys = (CPS * s + fq) ^ fsw;
+    fa_off[s] = (grp * WTM + frow) * kD2Row + phys * 8;
+    fb_off[s] = (w4 * WTN + frow) * kD2Row + phys * 8;
+  }
+  h8 fa[KSTEPS][FM], fb[KSTEPS][FN];
+  auto read_tile = [&](int ast, int bst) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int q = 0; q < FN; ++q)
+        fb[s][q] = *reinterpret_cast<const h8*>(lds + B_OFF + bst * B_STRIDE + fb_off[s] + q * MF * kD2Row);
+#pragma unroll
+      for (int q = 0; q < FM; ++q)
+        fa[s][q] = *reinterpret_cast<const h8*>(lds + ast * A_STRIDE + fa_off[s] + q * MF * kD2Row);
+    }
+  };
+
+  typename MM::acc_t acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int v = 0; v < MM::NACC; ++v) acc[fm][fn][v] = 0.0f;
+  auto multiply = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::mma(fb[s][fn], fa[s][fm], acc[fm][fn]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto wait_vm = [&](auto NC) {
+    constexpr int n = decltype(NC)::value;
+    static_assert(n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  };
+  using InFlightA = std::integral_constant<int, ring::pp_in_flight_a(A_BLK)>;
+  using InFlightB = std::integral_constant<int, ring::pp_in_flight_b(B_BLK)>;
+  using CopiesA = std::integral_constant<int, A_BLK>;
+  using None = std::integral_constant<int, 0>;
+
+  const int nk = (K + BK - 1) / BK;
+  // prologue: group 1 copies A tiles 0 and 1, group 0 B tile 0; tile 0 landed
+  if (grp == 1) {
+    copy_a(0, 0);
+    copy_a(1, 1);
+    wait_vm(CopiesA{});
+  } else {
+    copy_b(0, 0);
+    wait_vm(None{});
+  }
+  __syncthreads();
+  // Phases ph = -1 .. 2nk-1, each ended by a barrier.  Group 0 multiplies K
+  // tile ph / 2 in the even phases; in the odd ones it copies B tile
+  // (ph - 1) / 2 + 2 and reads its fragments of tile (ph + 1) / 2.  Group 1
+  // multiplies tile ph / 2 in the odd phases; in the even ones it copies A tile
+  // ph / 2 + 2 and reads its fragments of tile ph / 2.  Each group runs its
+  // own loop with one multiply and one read site, so that one set of fragment
+  // registers is live beside the accumulators.
+  if (grp == 0) {
+    copy_b(1, 1);  // phase -1: B tile 1, fragments of tile 0
+    read_tile(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      multiply();
+      wait_vm(InFlightB{});  // B of tile kt+1 has landed
+      __syncthreads();
+      const ring::Trip tr = ring::pp_trip(kt);
+      copy_b(tr.wb, tr.tb);
+      if (kt + 1 < nk) {
+        const ring::Trip nx = ring::pp_trip(kt + 1);
+        read_tile(nx.ra, nx.rb);
+      }
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();  // phase -1
+    for (int kt = 0; kt < nk; ++kt) {
+      const ring::Trip tr = ring::pp_trip(kt);
+      copy_a(tr.wa, tr.ta);
+      read_tile(tr.ra, tr.rb);
+      wait_vm(InFlightA{});  // A of tile kt+1 has landed (A of kt+2 may fly)
+      __syncthreads();
+      multiply();
+      __syncthreads();
+    }
+  }
+  wait_vm(None{});  // copies past the last tile drain before the scratch or the exit
+
+  char* Cw = static_cast<char*>(p.C) + m0 * ldc * 2;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  bool staged = false;
+  if constexpr (SC) {
+    constexpr int SCR_HALVES = 16 * WTN;
+    static_assert(8 * SCR_HALVES <= A_STRIDE, "staging scratch fits in an A stage");
+    if ((N & 7) == 0) {
+      staged = true;
+      __syncthreads();  // every wave's last copies have landed and its reads are done
+      store_c_staged<FM, FN, WTN>(acc, lds + 2 * A_STRIDE + wave * SCR_HALVES, rsc, grp * WTM,
+                                  n0 + w4 * WTN, N, ldc, lane, K <= 128);
+    }
+  }
+  // lane l holds, per MFMA block, output row l % MF and columns
+  // g * (256 / MF) + 4 * (l / MF) + e for g < NACC / 4, e < 4
+  if (staged) {
+  } else if ((N & 3) == 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = grp * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + w4 * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * g + e];
+          OpF16::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, v);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int i = grp * WTM + fm * MF + lane % MF;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int g = 0; g < MM::NACC / 4; ++g) {
+          const int j = n0 + w4 * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            OpF16::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
+                          acc[fm][fn][4 * g + e]);
+        }
+    }
+  }
+}
+template <int BM, int BN, int MF>
+__global__ void __launch_bounds__(512) pp2tile_kernel(GemmArgs p) {
+  pp2_body<BM, BN, false, MF>(p);
+}
+template <int BM, int BN>
+__global__ void __launch_bounds__(512) pp2tilesc_kernel(GemmArgs p) {
+  pp2_body<BM, BN, true>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -2124,6 +2367,19 @@ template <int BM, int BN>
 hipError_t launch_pptile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   hipLaunchKernelGGL((pptile_kernel<BM, BN>), dim3((unsigned)g), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int MF>
+hipError_t launch_pp2tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((pp2tile_kernel<BM, BN, MF>), dim3((unsigned)g), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN>
+hipError_t launch_pp2tilesc(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((pp2tilesc_kernel<BM, BN>), dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,27 @@ MIHG_RING_FN int k_in_flight(int S, int SB, int a_blk, int b_blk) {
   return a_blk * (S - 2) + b_blk * (SB - 2);
 }
 
+// pp2tile (two groups of waves taking turns at the matrix pipes, one full K
+// tile per turn): 3 stages of A, 2 of B, both copied two tiles ahead.  K tile
+// kt is read by group 0 in phase 2kt-1 and by group 1 in phase 2kt; group 1
+// copies A tile kt+2 in phase 2kt (into the stage tile kt-1 left), group 0
+// copies B tile kt+2 in phase 2kt+1 (into the stage tile kt leaves).
+MIHG_RING_FN Trip pp_trip(int kt) {
+  Trip t{};
+  t.ra = kt % 3;
+  t.rb = kt & 1;
+  t.wa = (kt + 2) % 3;
+  t.wb = kt & 1;
+  t.ta = kt + 2;
+  t.tb = kt + 2;
+  return t;
+}
+// pp2tile: copies a group's wave may leave in flight when its turn at the
+// matrix pipes or at memory ends: group 1 (A) the tile it just issued, group 0
+// (B) none, at the end of its compute phase (the tile issued a phase before).
+MIHG_RING_FN int pp_in_flight_a(int a_blk) { return a_blk; }
+MIHG_RING_FN int pp_in_flight_b(int) { return 0; }
+
 #undef MIHG_RING_FN
 
 }  // namespace ring

@@ -48,7 +48,7 @@ extern "C" {
 #endif
 
 #define MI_HGEMM_VERSION_MAJOR 0
-#define MI_HGEMM_VERSION_MINOR 1
+#define MI_HGEMM_VERSION_MINOR 2
 
 typedef struct mi_hgemm_ctx* mi_hgemm_handle_t;
 
@@ -147,7 +147,9 @@ mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int
  * C bit-identical to the element-wise instance's (a candidate that differs is
  * discarded); it is then timed on operands with random mantissas scaled by
  * 1/sqrt(K) (the clock under load depends on the data), as the median of 5
- * replays of a captured graph of repeated launches on a private stream.  The
+ * replays of a captured graph of repeated launches on a private stream; the
+ * three fastest are then re-timed in three interleaved rounds and the lowest
+ * median over each one's 15 replays wins.  The
  * launches rotate over enough copies of the operands and of the output to
  * overflow the 256 MiB MALL (at most 64 copies and 4 GiB), so each reads its
  * operands from HBM and writes its C past the MALL, as in real use.  The fastest correct one becomes the handle's entry for the shape.
@@ -158,7 +160,8 @@ mi_hgemm_status_t mi_hgemm_run_i8(mi_hgemm_handle_t h, int64_t M, int64_t N, int
  * Synchronises `stream`.  Allocates scratch (the operand sets and two
  * outputs, freed before returning).  With the environment variable
  * MI_HGEMM_TUNE_LOG set (and not "0"), every timed candidate is printed to
- * stderr as one line: M N K kernel g<group_m> x<xcd_remap> s<split> µs.
+ * stderr as one line: M N K kernel g<group_m> x<xcd_remap> s<split> µs, and
+ * each finalist as "final M N K kernel g x s median .. min .. max ..".
  * Returns OK, INVALID_ARG, UNSUPPORTED, NO_DEVICE, ERR_HIP or ERR_IO.
  */
 mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64_t N, int64_t K,

@@ -84,6 +84,21 @@ struct Replay {
       }
     ++seq;
   }
+  // the same for a wave that copies only operand `kind` (its vmcnt counts
+  // only those copies)
+  void wait_kind(int n, int kind) {
+    int k = -n;
+    for (const Copy& c : copies) k += c.kind == kind;
+    for (Copy& c : copies) {
+      if (c.kind != kind) continue;
+      if (k-- <= 0) break;
+      if (c.landed < 0) {
+        c.landed = epoch;
+        c.landed_seq = seq;
+      }
+    }
+    ++seq;
+  }
   void barrier() { ++epoch; }
 
   void hazard(const char* what, int a, int b) {
@@ -249,6 +264,59 @@ int replay_k(int BM, int BN, int NW, int WTN, int KB, int S, int SB, int nk, boo
   return r.hazards;
 }
 
+// pp2tile: two groups of waves in turn, BM x BN x 64 tiles, three A stages
+// and two B stages of 128-byte rows; group 1 copies A, group 0 copies B.  Each
+// phase's events of both groups fall into one epoch (barrier to barrier).
+int replay_pp(int BM, int BN, int WTN, int nk, bool sc) {
+  const int a_blk = BM / 8 / 4, b_blk = BN / 8 / 4, row = 128;
+  Replay r;
+  r.name = "pp2tile " + std::to_string(BM) + "x" + std::to_string(BN) + " nk " + std::to_string(nk) +
+           (sc ? " staged C" : "");
+  r.a_bytes = BM * row;
+  r.b_bytes = BN * row;
+  r.a_lo0 = 0, r.a_stride = BM * row, r.b_lo0 = 3 * BM * row, r.b_stride = BN * row;
+  const int in_a = mihg::ring::pp_in_flight_a(a_blk), in_b = mihg::ring::pp_in_flight_b(b_blk);
+  // prologue
+  r.copy(0, 0, 0, a_blk);  // group 1
+  r.copy(0, 1, 1, a_blk);
+  r.wait_kind(a_blk, 0);
+  r.copy(1, 0, 0, b_blk);  // group 0
+  r.wait_kind(0, 1);
+  r.barrier();
+  // phase -1: group 0 copies B tile 1 and reads tile 0
+  r.copy(1, 1, 1, b_blk);
+  r.read(0, 0, 0);
+  r.read(1, 0, 0);
+  r.barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const Trip t = mihg::ring::pp_trip(kt);
+    // phase 2kt: group 0 multiplies, then waits for B of kt+1; group 1 copies
+    // A of kt+2, reads tile kt, waits
+    r.wait_kind(in_b, 1);
+    r.copy(0, t.wa, t.ta, a_blk);
+    r.read(0, t.ra, kt);
+    r.read(1, t.rb, kt);
+    r.wait_kind(in_a, 0);
+    r.barrier();
+    // phase 2kt+1: group 1 multiplies; group 0 copies B of kt+2, reads kt+1
+    r.copy(1, t.wb, t.tb, b_blk);
+    if (kt + 1 < nk) {
+      const Trip n = mihg::ring::pp_trip(kt + 1);
+      r.read(0, n.ra, kt + 1);
+      r.read(1, n.rb, kt + 1);
+    }
+    r.barrier();
+  }
+  r.wait_kind(0, 0);
+  r.wait_kind(0, 1);
+  if (sc) {
+    r.barrier();
+    r.write(2 * BM * row, 2 * BM * row + 8 * 16 * WTN * 2, "staged-C scratch overlaps a pending copy or read");
+  }
+  r.check();
+  return r.hazards;
+}
+
 }  // namespace
 
 int main() {
@@ -284,6 +352,12 @@ int main() {
     for (int nk : nks)
       for (int split = 0; split < 2; ++split)
         for (int sc = 0; sc < 2; ++sc) note(replay_k(k.bm, k.bn, k.nw, k.wtn, k.kb, k.s, k.sb, nk, split, sc));
+  // pp2tile: (BM, BN, wave columns)
+  struct PP { int bm, bn, wtn; };
+  const PP pps[] = {{256, 256, 64}, {256, 192, 48}, {256, 128, 32}, {128, 256, 64}};
+  for (const PP& q : pps)
+    for (int nk : nks)
+      for (int sc = 0; sc < 2; ++sc) note(replay_pp(q.bm, q.bn, q.wtn, nk, sc));
   std::printf("replayed %d configurations, %d with hazards\n", configs, bad);
   return bad ? 1 : 0;
 }

@@ -147,12 +147,13 @@ def test_heuristic_picks_by_shape(inspect_handle):
         assert r[0] == mh.MI_HGEMM_OK
         return names[r[1]], r[4]
 
-    # three quarters of a wave or more of 256x256 tiles keeps the large tile
-    # (binary16 picks stage C through LDS for whole-line stores)
-    assert choice(8192, 8192, 8192) == ("d2tile3_256x256_w2x4_m16_sc", 1)
-    assert choice(8192, 8192, 64) == ("d2tile3_256x256_w2x4_m16_sc", 1)
-    assert choice(4096, 4096, 4096) == ("d2tile3_256x256_w2x4_m16_sc", 1)
-    assert choice(1024, 14336, 4096) == ("d2tile3_256x256_w2x4_m16_sc", 1)
+    # five eighths of a wave or more of 256x256 tiles keeps the large tile, in
+    # its ping-pong form (binary16 picks stage C through LDS for whole-line stores)
+    assert choice(8192, 8192, 8192) == ("pp2tile_256x256_w8_m16_sc", 1)
+    assert choice(8192, 8192, 64) == ("pp2tile_256x256_w8_m16_sc", 1)
+    assert choice(4096, 4096, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
+    assert choice(1024, 14336, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
+    assert choice(1024, 11008, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
     # below that, two waves or more of 128x128 direct-to-LDS tiles, at any K
     assert choice(2048, 4096, 64) == ("d2tile_128x128_w2x2_m16_sc", 1)
     assert choice(2048, 4096, 4096) == ("d2tile_128x128_w2x2_m16_sc", 1)

@@ -2,9 +2,10 @@
 
 tests/ring_model.cpp replays the stage functions the kernels use
 (dense_fp16_gemm_hgemm_amd/csrc/ring_schedule.h) over whole K loops of the
-d2tile (two A stages), d2tile3 (three A stages), persistent d2tile3 and ktile
-rings, with the staged-C scratch and the split-K flag word, and reports every
-read of a stage before its copies have landed, every refill of a stage while
+d2tile (two A stages), d2tile3 (three A stages), persistent d2tile3, ktile
+and pp2tile (two groups of waves in turn) rings, with the staged-C scratch and
+the split-K flag word, and reports every read of a stage before its copies
+have landed, every refill of a stage while
 it is still read, two copies into one stage in flight together, and scratch
 written over LDS still in use.  The shipped functions must replay with no
 hazard; copies of them with one planted mistake each (a stage index one off,
@@ -36,6 +37,12 @@ MUTANTS = {
     "k_b_copy_one_tile_long": ("t.tb = kt + SB - 1;", "t.tb = kt + SB;"),
     "k_wait_leaves_a_trip_more": ("return a_blk * (S - 2) + b_blk * (SB - 2);",
                                   "return a_blk * (S - 1) + b_blk * (SB - 2);"),
+    "pp_a_refills_the_stage_being_read": ("t.wa = (kt + 2) % 3;", "t.wa = (kt + 1) % 3;"),
+    "pp_b_refills_the_next_tiles_stage": ("t.wb = kt & 1;", "t.wb = (kt + 1) & 1;"),
+    "pp_a_wait_one_tile_short": ("MIHG_RING_FN int pp_in_flight_a(int a_blk) { return a_blk; }",
+                                 "MIHG_RING_FN int pp_in_flight_a(int a_blk) { return 2 * a_blk; }"),
+    "pp_b_wait_leaves_a_copy": ("MIHG_RING_FN int pp_in_flight_b(int) { return 0; }",
+                                "MIHG_RING_FN int pp_in_flight_b(int) { return 1; }"),
     "k_a_copies_issued_first": ("MIHG_RING_FN bool k_b_first(int S, int SB) { return SB != S; }",
                                 "MIHG_RING_FN bool k_b_first(int S, int SB) { return S != S + SB - SB; }"),
 }
