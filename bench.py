@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--mnk", default=None, help="custom shape M_N_K (randn/sqrt(K) inputs)")
     ap.add_argument("--warm", action="store_true", help="reuse one operand set (MALL-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the live MFMA / HBM ceiling probes (libmi_ceiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--all-configs", default=None,
@@ -79,25 +81,10 @@ def parse():
     return ap.parse_args()
 
 
-# the device code of the kernels (host dispatch code and tables are not part of it)
-DEVICE_SOURCES = ("kernels.hpp", "instances.hip", "internal.h")
-
-
-def _code_only(text: str) -> str:
-    """C++ source without comments and blank lines (comments do not change the kernels)."""
-    import re
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
-
-
 def source_digest() -> str:
-    h = hashlib.sha256()
-    for name in DEVICE_SOURCES:
-        with open(os.path.join(ROOT, "dense_fp16_gemm_hgemm_amd", "csrc", name), encoding="utf-8") as fh:
-            h.update(name.encode())
-            h.update(_code_only(fh.read()).encode())
-    return h.hexdigest()[:16]
+    """Digest of the device sources' code (comments and blank lines removed)."""
+    from dense_fp16_gemm_hgemm_amd.provenance import source_digest as digest
+    return digest()
 
 
 def load_traffic(kernel: str, workload: str, group_m: int, xcd_remap: int, split_k: int):
@@ -226,6 +213,72 @@ def roofline(p, launch_ms, kernel, workload, raster=(1, 0, 1)):
             "algorithmic_flops": flops, "algorithmic_bytes": nbytes}
 
 
+def practical_ceiling(roof, p):
+    """libmi_ceiling's live measurement beside the published peak: for an
+    MFMA-bound launch the MFMA-only rate on random fp16 (int8 work is compared
+    at twice that rate, the int8 MFMA doing twice the operations per cycle),
+    for an HBM-bound one the streaming read rate."""
+    from dense_fp16_gemm_hgemm_amd import ceiling
+    m = ceiling.measure()
+    if roof["bound"] == "mfma":
+        ceil = m["mfma_tflops"] * (2 if p.kind == "i8" else 1)
+        unit = roof["unit"]
+    else:
+        ceil, unit = m["hbm_read_gbs"], "GB/s"
+    m.update({"value": ceil, "unit": unit, "frac": round(roof["achieved"] / ceil, 4)})
+    return m
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+SINGLE_CORE_SNIPPET = r"""
+import json, sys, time
+import numpy as np
+sys.path.insert(0, {root!r})
+import oracle
+from dense_fp16_gemm_hgemm_amd import inputs
+p = inputs.Problem("single_core", {rows}, {N}, {K}, {kind!r}, {a_scale!r}, {b_scale!r}, {seed})
+A, Bt = inputs.make(p)
+orc = oracle.default()
+orc.set_num_threads(1)
+f = orc.igemm_tn if p.kind == "i8" else orc.hgemm_tn
+f(A[:1], Bt[:64])
+t0 = time.perf_counter()
+f(A, Bt)
+t = time.perf_counter() - t0
+print(json.dumps({{"threads": orc.num_threads(), "seconds": t, "flop": 2.0 * p.M * p.N * p.K}}))
+"""
+
+
+def single_core_oracle(p, target_s=3.0):
+    """The oracle on one host core (one OpenMP thread, set through the oracle
+    library itself, in a child process that never touches the GPU), on the
+    first rows of the same problem; "threads" is what the library reports."""
+    import subprocess
+    rows = max(1, min(p.M, int(target_s * 4e9 / (2 * p.N * p.K))))
+    code = SINGLE_CORE_SNIPPET.format(root=ROOT, rows=rows, N=p.N, K=p.K, kind=p.kind,
+                                      a_scale=p.a_scale, b_scale=p.b_scale, seed=p.seed)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                           timeout=120)
+        d = json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:  # reported, never fatal to the bench line
+        return {"error": str(e)[:200]}
+    return {"value": round(d["flop"] / d["seconds"] / 1e12, 6), "threads": d["threads"],
+            "seconds": round(d["seconds"], 3),
+            "sample": f"{rows}x{p.N}x{p.K} ({rows} rows of the workload, same distribution and seed)"}
+
+
 def cpu_baseline(p, A, Bt, gpu_c, target_s):
     """The oracle, as it is, on rows 0..R-1 of the product; R sized to ~target_s."""
     import numpy as np
@@ -260,7 +313,7 @@ def cpu_baseline(p, A, Bt, gpu_c, target_s):
         bound = 1e-3 * np.abs(r64[fin]).max() + 2e-3 * np.abs(r64[fin])
         ok = bool(np.all(np.abs(g[fin] - r64[fin]) <= bound))
     return {"value": round(flop / t / 1e12, 6), "unit": "TOP/s" if i8 else "TFLOP/s",
-            "cores": orc.num_threads(),
+            "cores": orc.num_threads(), "cpu_model": cpu_model(),
             "kind": "oracle", "seconds": round(t, 3),
             "sample": f"rows 0..{R - 1} of C ({R}x{p.N} outputs, K={p.K}) of {p.name}",
             "sample_parity": "ok" if ok else "FAIL"}
@@ -338,10 +391,12 @@ def measure(lib, p, steps, warmup, cold, with_torch=False, force=None, device_ti
         def run(a, b, c):
             lib.run_kernel(kernel, a, b, c, group_m=gm, xcd_remap=xcd, split_k=sk)
     ms, launch_ms, wall, per = time_steps(run, wl, steps, warmup)
+    q = statistics.quantiles(per, n=4) if len(per) >= 2 else [per[0]] * 3
     rec = {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "kernel": kernel, "group_m": gm,
            "xcd_remap": xcd, "split_k": sk, "cache": "cold" if cold else "warm", "sets": len(wl.sets),
            "ms_per_step": ms, "us_per_call": round(launch_ms * 1e3, 3),
            "us_per_call_median": round(statistics.median(per) * 1e3, 3),
+           "us_per_call_iqr": [round(q[0] * 1e3, 3), round(q[2] * 1e3, 3)],
            "tflops": round(p.flops / (ms * 1e-3) / 1e12, 3), "wall_s": wall,
            "roofline": roofline(p, launch_ms, kernel, p.name, (gm, xcd, sk))}
     if with_torch:
@@ -567,6 +622,7 @@ def main():
                    "group_m": rec["group_m"], "xcd_remap": rec["xcd_remap"],
                    "split_k": rec["split_k"], "dispatch": "forced" if args.kernel else "library",
                    "us_per_call": rec["us_per_call"], "us_per_call_median": rec["us_per_call_median"],
+                   "us_per_call_iqr": rec["us_per_call_iqr"],
                    "parallelism": "none (1 GPU)"},
         "roofline": rec["roofline"],
         "cpu_baseline": None,
@@ -588,10 +644,17 @@ def main():
             "device_roofline_bound": rs["device_roofline"]["bound"],
             "torch_device_us_per_call": rs.get("torch_device_us_per_call")}
         torch.cuda.empty_cache()
+    if not args.no_ceiling:
+        # the chip's practical ceilings, measured now (after the timed region):
+        # MFMA-only on random operands with the clock under that load, and the
+        # streaming HBM read rate; the kernel's rate as a fraction of each
+        out["roofline"]["practical_ceiling"] = practical_ceiling(out["roofline"], p)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         gpu_c = wl.sets[(args.steps - 1) % len(wl.sets)][2].cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(p, wl.A_host, wl.Bt_host, gpu_c, args.cpu_seconds)
+        out["cpu_baseline"]["single_core"] = single_core_oracle(p)
     lib.close()
     print(json.dumps(out), flush=True)
 

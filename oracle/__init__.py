@@ -97,6 +97,8 @@ class Oracle:
         lib.ref_fma_chain.restype = ctypes.c_int
         lib.ref_fma_chain.argtypes = [p, p, i64, ctypes.c_int32, ctypes.c_float, ctypes.c_float]
         lib.ref_num_threads.restype = ctypes.c_int
+        lib.ref_set_num_threads.restype = None
+        lib.ref_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
         self.path = lib_path
 
@@ -233,6 +235,12 @@ class Oracle:
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.ref_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the oracle's later parallel loops (n >= 1)."""
+        if n < 1:
+            raise ValueError("n must be at least 1")
+        self.lib.ref_set_num_threads(int(n))
 
 
 _default: Oracle | None = None

@@ -256,3 +256,15 @@ int ref_num_threads(void)
     return 1;
 #endif
 }
+
+/* Set the threads of this library's later parallel regions (n >= 1): the
+   environment does not always reach the OpenMP runtime this library links. */
+void ref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
