@@ -75,6 +75,10 @@ namespace mihg {
   X(256, 256)                       \
   X(256, 128)                       \
   X(128, 256)
+// PP2TILESK: X(BM, BN): PP2TILESC splitting K (few output tiles, long K)
+#define MIHG_PP2TILESK_INSTANCES(X) \
+  X(256, 256)                       \
+  X(256, 128)
 
 // Int8 variant (int8 operands, int32 results).  I8_D2TILE: X(BM, BN, WGM, WGN),
 // K step 128; I8_KTILE: X(BM, BN, WGM, WGN, BK, S), K step BK of 256 or 512.
@@ -206,6 +210,7 @@ namespace mihg {
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_PP2TILE(BM, BN) template __global__ void pp2tile_kernel<BM, BN, 16>(GemmArgs);
 #define INSTANTIATE_PP2TILESC(BM, BN) template __global__ void pp2tilesc_kernel<BM, BN>(GemmArgs);
+#define INSTANTIATE_PP2TILESK(BM, BN) template __global__ void pp2tilesc_kernel<BM, BN, true>(GemmArgs);
 #define INSTANTIATE_KTILE(BM, BN, WGM, WGN, BK, S) \
   template __global__ void ktile_kernel<BM, BN, WGM, WGN, BK / 64, S, S>(GemmArgs);
 #define INSTANTIATE_KTILE_B(BM, BN, WGM, WGN, BK, S, SB) \
@@ -242,6 +247,7 @@ MIHG_D2TILE3_INSTANCES(INSTANTIATE_D2TILE3)
 MIHG_PPTILE_INSTANCES(INSTANTIATE_PPTILE)
 MIHG_PP2TILE_INSTANCES(INSTANTIATE_PP2TILE)
 MIHG_PP2TILESC_INSTANCES(INSTANTIATE_PP2TILESC)
+MIHG_PP2TILESK_INSTANCES(INSTANTIATE_PP2TILESK)
 MIHG_KTILE_INSTANCES(INSTANTIATE_KTILE)
 MIHG_KTILE_B_INSTANCES(INSTANTIATE_KTILE_B)
 MIHG_KTILE_NT_INSTANCES(INSTANTIATE_KTILE_NT)
@@ -289,6 +295,9 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
 #define PP2TILESC_DESC(BM, BN)                                                             \
   {"pp2tile_" #BM "x" #BN "_w8_m16_sc", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                 \
    (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_pp2tilesc<BM, BN>, &grid_tile<BM, BN>},
+#define PP2TILESK_DESC(BM, BN)                                                             \
+  {"pp2tile_" #BM "x" #BN "_w8_m16_sc_sk", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,              \
+   (3 * BM + 2 * BN) * kD2Row * 2, 1, &launch_pp2tilesc<BM, BN, true>, &grid_tile<BM, BN>},
 #define KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1,                                             \
@@ -355,6 +364,7 @@ const KernelDesc kKernels[] = {
     MIHG_PPTILE_INSTANCES(PPTILE_DESC)
     MIHG_PP2TILE_INSTANCES(PP2TILE_DESC)
     MIHG_PP2TILESC_INSTANCES(PP2TILESC_DESC)
+    MIHG_PP2TILESK_INSTANCES(PP2TILESK_DESC)
     MIHG_KTILE_INSTANCES(KTILE_DESC)
     MIHG_KTILE_B_INSTANCES(KTILE_B_DESC)
     MIHG_KTILE_NT_INSTANCES(KTILE_NT_DESC)

@@ -533,7 +533,11 @@ __device__ __forceinline__ void dtrip_schedule() {
 // past the XCD's L2), every wave waits until its stores are acknowledged
 // before the workgroup counts itself in, and the counter is a device-scope
 // atomic.  The last slice reads the partials only after its atomic returned.
-template <int FM, int FN, int NT, typename Acc>
+// VGMAX caps the 16-byte loads a lane keeps in flight while summing (its
+// registers sit beside the accumulators).  REREAD: the last slice reads its
+// own partial back like the others instead of keeping it in registers, so the
+// accumulators are free while it sums (for register-bound instances).
+template <int FM, int FN, int NT, int VGMAX = 16, bool REREAD = false, typename Acc>
 __device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs& p, int tile_id,
                                              int slice, int splitk, int tid, int* s_last) {
   typedef std::remove_cv_t<std::remove_reference_t<decltype(acc[0][0][0])>> E;  // float or int
@@ -567,7 +571,7 @@ __device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs&
   if (!*s_last) return false;
   // running sum over slices 0..splitk-1 in order, VG float4 values per lane
   // at a time; a slice's VG loads are issued together before any is added
-  constexpr int VG = NV < 16 ? NV : 16;
+  constexpr int VG = NV < VGMAX ? NV : VGMAX;
   static_assert(NV % VG == 0, "whole groups");
 #pragma unroll
   for (int v0 = 0; v0 < NV; v0 += VG) {
@@ -575,7 +579,7 @@ __device__ __forceinline__ bool splitk_fixup(Acc (&acc)[FM][FN], const GemmArgs&
 #pragma unroll
     for (int u = 0; u < VG; ++u) sum[u] = f4{0, 0, 0, 0};
     for (int s2 = 0; s2 < splitk; ++s2) {
-      if (s2 == slice) {
+      if (!REREAD && s2 == slice) {
 #pragma unroll
         for (int u = 0; u < VG; ++u) {
           const int v = v0 + u, fg = v / (NACC / 4), g = v % (NACC / 4);
@@ -1532,7 +1536,9 @@ pptile_kernel(GemmArgs p) {
 // ends each memory phase with its previous A tile landed, group 0 each
 // compute phase with its previous B tile landed, so tile kt+1 is complete
 // before the barrier that opens its first reads (phase 2kt+1).
-template <int BM, int BN, bool SC, int MF = 16>
+// SK: the instance splits K (GemmArgs::splitk slices, the shared fix-up);
+// without it the slice bookkeeping compiles away.
+template <int BM, int BN, bool SC, int MF = 16, bool SK = false>
 __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
   using MM = Mfma<MF>;
   constexpr int BK = 64, KSTEPS = BK / MM::KI, CPS = MM::KI / 8;  // CPS: 16-byte chunks per k-step
@@ -1552,22 +1558,32 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int w4 = __builtin_amdgcn_readfirstlane(wave & 3);
   const int M = p.M, N = p.N, K = p.K;
+  // split-K: workgroup id = tile * splitk + slice; slice s covers K range
+  // [s * kchunk, min(K, (s + 1) * kchunk)), kchunk a multiple of 64
+  // (the division runs on the vector unit: its uniform results are moved back
+  // to scalar registers, where everything derived from them stays)
+  const int splitk = SK ? p.splitk : 1;
+  const int tile_id = __builtin_amdgcn_readfirstlane(blockIdx.x / splitk);
+  const int slice = __builtin_amdgcn_readfirstlane(blockIdx.x - tile_id * splitk);
+  const int k_begin = splitk > 1 ? slice * p.kchunk : 0;
+  const int KS = splitk > 1 ? min(p.kchunk, K - k_begin) : K;  // this slice's depth
   int tm, tn;
-  tile_coords(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
+  tile_coords(tile_id, (M + BM - 1) / BM, (N + BN - 1) / BN, p.group_m, p.xcd_remap, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t lda = p.lda, ldb = p.ldb, ldc = p.ldc;
 
   // copies: lane l -> row l/8 of an 8-row block, physical chunk l%8, which
-  // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1))
+  // holds logical chunk (l%8) ^ ((l>>4) ^ 4*(block&1)).  The operand views
+  // start at the slice's first k and end where the full rows end.
   const int drow = lane >> 3;
   const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
-  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda,
-                             (uint32_t)(min(BM, M - m0) * lda * 2));
-  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb,
-                             (uint32_t)(min(BN, N - n0) * ldb * 2));
+  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda + k_begin,
+                             (uint32_t)((min(BM, M - m0) * lda - k_begin) * 2));
+  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb + k_begin,
+                             (uint32_t)((min(BN, N - n0) * ldb - k_begin) * 2));
   const int64_t ldx = grp == 1 ? lda : ldb;
   const uint32_t v0 = (uint32_t)(drow * ldx * 2 + dch0 * 16), v1 = (uint32_t)(drow * ldx * 2 + dch1 * 16);
-  const bool mask_k = (K & 63) != 0;
+  const bool mask_k = (KS & 63) != 0;
   const uint32_t lds0 = lds_addr(lds);
   // this wave's copies of K tile t: group 1 copies its quarter of A's rows into
   // A stage `st` (copy_a), group 0 its quarter of B's rows into B stage `st`
@@ -1577,7 +1593,7 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
 #pragma unroll
     for (int x = 0; x < A_BLK; ++x) {
       const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (t * BK + ch * 8 < K);
+      const bool kin = !mask_k || (t * BK + ch * 8 < KS);
       const int blk = w4 * A_BLK + x;
       dma16(rda, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
             lds0 + (uint32_t)((st * A_STRIDE + blk * 8 * kD2Row) * 2));
@@ -1588,7 +1604,7 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
 #pragma unroll
     for (int x = 0; x < B_BLK; ++x) {
       const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (t * BK + ch * 8 < K);
+      const bool kin = !mask_k || (t * BK + ch * 8 < KS);
       const int blk = w4 * B_BLK + x;
       dma16(rdb, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
             lds0 + (uint32_t)((B_OFF + st * B_STRIDE + blk * 8 * kD2Row) * 2));
@@ -1644,7 +1660,7 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
   using CopiesA = std::integral_constant<int, A_BLK>;
   using None = std::integral_constant<int, 0>;
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (KS + BK - 1) / BK;
   // prologue: group 1 copies A tiles 0 and 1, group 0 B tile 0; tile 0 landed
   if (grp == 1) {
     copy_a(0, 0);
@@ -1691,6 +1707,15 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
     }
   }
   wait_vm(None{});  // copies past the last tile drain before the scratch or the exit
+
+  if constexpr (SK) {
+    // the flag word reuses LDS word 0 (A stage 0): the fix-up writes it only
+    // after a barrier that follows every wave's last fragment read and its
+    // drained copies; the staged-C scratch below lies in A stage 2
+    if (splitk > 1 && !splitk_fixup<FM, FN, 512, 16, true>(acc, p, tile_id, slice, splitk, tid,
+                                                           reinterpret_cast<int*>(lds)))
+      return;
+  }
 
   char* Cw = static_cast<char*>(p.C) + m0 * ldc * 2;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
@@ -1740,13 +1765,13 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
     }
   }
 }
-template <int BM, int BN, int MF>
+template <int BM, int BN, int MF, bool SK = false>
 __global__ void __launch_bounds__(512) pp2tile_kernel(GemmArgs p) {
-  pp2_body<BM, BN, false, MF>(p);
+  pp2_body<BM, BN, false, MF, SK>(p);
 }
-template <int BM, int BN>
+template <int BM, int BN, bool SK = false>
 __global__ void __launch_bounds__(512) pp2tilesc_kernel(GemmArgs p) {
-  pp2_body<BM, BN, true>(p);
+  pp2_body<BM, BN, true, 16, SK>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -2370,16 +2395,16 @@ hipError_t launch_pptile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int MF>
+template <int BM, int BN, int MF, bool SK = false>
 hipError_t launch_pp2tile(const GemmArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((pp2tile_kernel<BM, BN, MF>), dim3((unsigned)g), dim3(512), 0, s, a);
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (SK ? a.splitk : 1);
+  hipLaunchKernelGGL((pp2tile_kernel<BM, BN, MF, SK>), dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
-template <int BM, int BN>
+template <int BM, int BN, bool SK = false>
 hipError_t launch_pp2tilesc(const GemmArgs& a, hipStream_t s) {
-  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((pp2tilesc_kernel<BM, BN>), dim3((unsigned)g), dim3(512), 0, s, a);
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (SK ? a.splitk : 1);
+  hipLaunchKernelGGL((pp2tilesc_kernel<BM, BN, SK>), dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -33,12 +33,13 @@ def mangled(name):
     if m:
         bm, bn, wm, wn, mf = m.groups()
         return f"_ZN4mihg14d2tile3_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}ELi{mf}EEEvNS_8GemmArgsE"
-    m = re.fullmatch(r"pp2tile_(\d+)x(\d+)_w8_m(\d+)(_sc)?", name)
+    m = re.fullmatch(r"pp2tile_(\d+)x(\d+)_w8_m(\d+)(_sc)?(_sk)?", name)
     if m:
-        bm, bn, mf, sc = m.groups()
+        bm, bn, mf, sc, sk = m.groups()
+        b = 1 if sk else 0
         if sc:
-            return f"_ZN4mihg16pp2tilesc_kernelILi{bm}ELi{bn}EEEvNS_8GemmArgsE"
-        return f"_ZN4mihg14pp2tile_kernelILi{bm}ELi{bn}ELi{mf}EEEvNS_8GemmArgsE"
+            return f"_ZN4mihg16pp2tilesc_kernelILi{bm}ELi{bn}ELb{b}EEEvNS_8GemmArgsE"
+        return f"_ZN4mihg14pp2tile_kernelILi{bm}ELi{bn}ELi{mf}ELb{b}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"pptile_(\d+)x(\d+)_w8_m16", name)
     if m:
         bm, bn = m.groups()

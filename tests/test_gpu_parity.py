@@ -407,7 +407,8 @@ SPLIT_KERNELS = ["dtile_128x128_w2x2_m16_s4", "dtile_256x128_w2x2_m16_s4",
                  "ktile_128x128_w2x2_k128_s2", "ktile_128x128_w2x4_k128_s3b2",
                  "ktile_16x64_w1x4_k256_s3_nt", "ktile_64x64_w2x2_k128_s3_nt",
                  "ktile_128x128_w2x4_k128_s3b2_noxor", "ktile_128x128_w2x4_k128_s3b2_sc",
-                 "ktile_64x64_w2x2_k128_s3b3_sc"]
+                 "ktile_64x64_w2x2_k128_s3b3_sc", "pp2tile_256x256_w8_m16_sc_sk",
+                 "pp2tile_256x128_w8_m16_sc_sk"]
 
 
 @pytest.mark.parametrize("kernel", SPLIT_KERNELS)
