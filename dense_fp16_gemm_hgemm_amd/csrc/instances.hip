@@ -297,7 +297,8 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
    (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_pp2tilesc<BM, BN>, &grid_tile<BM, BN>},
 #define PP2TILESK_DESC(BM, BN)                                                             \
   {"pp2tile_" #BM "x" #BN "_w8_m16_sc_sk", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,              \
-   (3 * BM + 2 * BN) * kD2Row * 2, 1, &launch_pp2tilesc<BM, BN, true>, &grid_tile<BM, BN>},
+   (3 * BM + 2 * BN) * kD2Row * 2, 1, &launch_pp2tilesc<BM, BN, true>, &grid_tile<BM, BN>,   \
+   DTYPE_F16, 1},
 #define KTILE_DESC(BM, BN, WGM, WGN, BK, S)                                                 \
   {"ktile_" #BM "x" #BN "_w" #WGM "x" #WGN "_k" #BK "_s" #S, FAMILY_TILE, BM, BN, BK,          \
    WGM * WGN, 16, 1, 1, S * (BM + BN) * BK * 2, 1,                                             \

@@ -49,6 +49,7 @@ struct KernelDesc {
   hipError_t (*launch)(const GemmArgs&, hipStream_t);
   int64_t (*grid)(int32_t M, int32_t N);  // workgroups for an M x N output
   int32_t dtype = DTYPE_F16;
+  int32_t split_only = 0;  // 1: a split-K twin of another instance; the tuner times it split only
 };
 
 extern const KernelDesc kKernels[];

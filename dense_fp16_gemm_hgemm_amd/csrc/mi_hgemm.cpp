@@ -991,7 +991,10 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     const KernelDesc& kd = kKernels[k];
     if (!kd.aligned || kd.dtype != dtype) continue;
     if (kd.grid((int32_t)M, (int32_t)N) > INT32_MAX) continue;
-    if (kd.family == mihg::FAMILY_TILE) {
+    if (kd.split_only) {
+      // unsplit, it is the same kernel as its twin plus unused bookkeeping
+      add_splits(k);
+    } else if (kd.family == mihg::FAMILY_TILE) {
       static const int rasters[][2] = {{1, 0}, {4, 0}, {8, 0}, {16, 0}, {1, 1}, {4, 1}, {8, 1}, {16, 1}};
       for (const auto& r : rasters) {
         if (heuristic_only && !((r[0] == 8 && r[1] == 1) || (r[0] == 1 && r[1] == 0))) continue;

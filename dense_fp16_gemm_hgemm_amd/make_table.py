@@ -2,7 +2,7 @@
 
     python -m dense_fp16_gemm_hgemm_amd.make_table [--out PATH] [--fresh] [--all]
                                                    [--heuristic] [--shapes M_N_K ...]
-                                                   [--int8] [--evidence PATH]
+                                                   [--int8] [--evidence PATH] [--log PATH]
 
 For every shape, ``mi_hgemm_tune`` times each compiled instance, raster setting
 and K split on the current GPU (exhaustive unless ``--heuristic``), re-times
@@ -93,6 +93,8 @@ def main(argv=None):
     ap.add_argument("--shapes", nargs="*", default=None, metavar="M_N_K")
     ap.add_argument("--int8", action="store_true", help="tune the int8 variant")
     ap.add_argument("--all", action="store_true", help="tune the fp16 and the int8 default shapes")
+    ap.add_argument("--log", default=None, metavar="PATH",
+                    help="also write the tuner's log (every timed candidate) to PATH")
     args = ap.parse_args(argv)
 
     import torch
@@ -112,11 +114,15 @@ def main(argv=None):
     h = Hgemm(table_path=table)
     base = MI_HGEMM_TUNE_HEURISTIC if args.heuristic else MI_HGEMM_TUNE_EXHAUSTIVE
     evidence = []
+    logf = open(args.log, "w", encoding="utf-8") if args.log else None
     try:
         for (M, N, K), int8 in jobs:
             t0 = time.perf_counter()
             flags = base | (MI_HGEMM_TUNE_INT8 if int8 else 0)
             log = tune_logged(h, M, N, K, flags)
+            if logf:
+                logf.write(log)
+                logf.flush()
             dev = torch.device("cuda", 0)
             et = torch.int8 if int8 else torch.float16
             a = torch.empty((M, K), dtype=et, device=dev)
@@ -151,6 +157,8 @@ def main(argv=None):
         print(f"wrote the evidence to {ev}", flush=True)
     finally:
         h.close()
+        if logf:
+            logf.close()
 
 
 def write_evidence(path, evidence, gpu_name):
