@@ -326,16 +326,18 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   // ping-pong tile (two wave groups taking turns at the matrix pipes) measured
   // 4-14% ahead of d2tile3 from 172 tiles up (1024x11008x4096 .. 8192^3)
   const int kpp = i8 ? -1 : find_kernel("pp2tile_256x256_w8_m16_sc");
-  // binary16 with 96 to 159 tiles of 256x128 over a K of 8192 or more: the
-  // ping-pong 256x128 tile, K split in two (1024x4096x11008 cold: 99.8 against
-  // 108.2 us for the deep-K 128x128 tile)
+  // binary16 with 96 to 159 tiles of 256x128 over a K of 8192 or more and an
+  // N of 2048 or more: the ping-pong 256x128 tile, K split in two
+  // (1024x4096x11008 cold: 99.8 against 108.2 us for the deep-K 128x128
+  // tile; 512x8192x8192: 81.0 against 84.6 us; at N = 512 it lost, 99.6
+  // against 82.0 us on 8192x512x8192)
   const int kppsk = i8 ? -1 : find_kernel("pp2tile_256x128_w8_m16_sc_sk");
   int64_t chunk2 = K;
   if (M > 64 && kpp >= 0 && tiles(kpp) >= 160) {
     pick(kpp, 1, 0, 1);
   } else if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
     pick(k256, 8, 1, 1);
-  } else if (M > 64 && kppsk >= 0 && K >= 8192 && tiles(kppsk) >= 96 && tiles(kppsk) < 160 &&
+  } else if (M > 64 && N >= 2048 && kppsk >= 0 && K >= 8192 && tiles(kppsk) >= 96 && tiles(kppsk) < 160 &&
              effective_split(kKernels[kppsk], M, N, K, 2, &chunk2) == 2) {
     pick(kppsk, 1, 0, 2);
   } else if (M > 64 && k128d >= 0 && tiles(k128d) >= 512) {

@@ -156,6 +156,7 @@ def test_heuristic_picks_by_shape(inspect_handle):
     assert choice(1024, 11008, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
     # 96..159 tiles of 256x128 over a long K: the same tile split in two along K
     assert choice(1024, 4096, 11008) == ("pp2tile_256x128_w8_m16_sc_sk", 2)
+    assert choice(8192, 512, 8192)[0] != "pp2tile_256x128_w8_m16_sc_sk"   # narrow N
     # below that, two waves or more of 128x128 direct-to-LDS tiles, at any K
     assert choice(2048, 4096, 64) == ("d2tile_128x128_w2x2_m16_sc", 1)
     assert choice(2048, 4096, 4096) == ("d2tile_128x128_w2x2_m16_sc", 1)
