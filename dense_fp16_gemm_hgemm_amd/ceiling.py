@@ -1,5 +1,5 @@
-"""Binding of libmi_ceiling: the practical MFMA, global -> LDS copy and HBM
-read ceilings of one MI355X, measured live (operation and exact results:
+"""Binding of libmi_ceiling: the practical MFMA, global -> LDS copy (from HBM
+and from L2) and HBM read ceilings of one MI355X, measured live (operation and exact results:
 ``include/mi_ceiling.h``).
 
 ``measure()`` runs the three probes on the current device and returns their
@@ -27,6 +27,8 @@ _lib.mi_ceiling_mfma.restype = ctypes.c_int
 _lib.mi_ceiling_mfma.argtypes = [_p, _i32, _i32, _p, _p, _p, _IP]
 _lib.mi_ceiling_copy_lds.restype = ctypes.c_int
 _lib.mi_ceiling_copy_lds.argtypes = [_p, _i64, _i32, _p, _p, _IP]
+_lib.mi_ceiling_copy_lds_cycle.restype = ctypes.c_int
+_lib.mi_ceiling_copy_lds_cycle.argtypes = [_p, _i64, _i32, _i32, _p, _p, _IP]
 _lib.mi_ceiling_read.restype = ctypes.c_int
 _lib.mi_ceiling_read.argtypes = [_p, _i64, _i32, _p, _p, _IP]
 
@@ -79,6 +81,18 @@ def copy_lds(src: torch.Tensor, workgroups: int, out: torch.Tensor | None = None
     return out
 
 
+def copy_lds_cycle(src: torch.Tensor, workgroups: int, trips: int, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """out[g] = XOR of the 32-bit words of 64 KiB trips (g + t) mod T, t < trips, of src."""
+    if out is None:
+        out = torch.empty(workgroups, dtype=torch.int32, device=src.device)
+    err = ctypes.c_int(0)
+    st = _lib.mi_ceiling_copy_lds_cycle(src.data_ptr(), src.numel() * src.element_size(), workgroups,
+                                        trips, out.data_ptr(), _stream(stream), ctypes.byref(err))
+    _check(st, err, "mi_ceiling_copy_lds_cycle")
+    return out
+
+
 def read(src: torch.Tensor, workgroups: int, out: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
     """out[g] = XOR of the 32-bit words of workgroup g's share of src, read into registers."""
@@ -108,8 +122,8 @@ def measure(device=None, mfma_iters: int = 4096, read_mib: int = 1024, copy_mib:
     """The three practical ceilings on `device` (default: the current one):
     MFMA-only TFLOP/s on random-mantissa operands (as the GEMM sees them; the
     clock depends on the data) with the measured shader clock, the global ->
-    LDS copy rate, and the streaming HBM read rate of a buffer four times the
-    256 MiB MALL."""
+    LDS copy rate, the rate at which one CU copies from L2 into its LDS, and
+    the streaming HBM read rate of a buffer four times the 256 MiB MALL."""
     dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
     g = torch.Generator(device=dev).manual_seed(1)
     frags = (torch.rand(FRAG_HALVES, device=dev, generator=g) * 2 - 1).half()
@@ -132,6 +146,15 @@ def measure(device=None, mfma_iters: int = 4096, read_mib: int = 1024, copy_mib:
     cms = _time_ms(lambda: copy_lds(src, cwgs, cout), 5)
     del src
 
+    # per-CU feed from L2: one 4-wave workgroup per CU cycling through 2 MiB
+    small = torch.empty((2 << 20) // 4, dtype=torch.int32, device=dev)
+    small.random_(generator=g)
+    l2trips = 256
+    lout = torch.empty(cus, dtype=torch.int32, device=dev)
+    lms = _time_ms(lambda: copy_lds_cycle(small, cus, l2trips, lout), 5)
+    lbytes = cus * l2trips * TRIP
+    del small
+
     rbytes = read_mib << 20
     rwgs = cus * 8
     rbytes -= rbytes % (rwgs * 4096)
@@ -145,11 +168,13 @@ def measure(device=None, mfma_iters: int = 4096, read_mib: int = 1024, copy_mib:
         "mfma_frac_of_peak": round(mfma_tflops / PEAK_MFMA_TFLOPS, 4),
         "clock_ghz_under_mfma": None if clock_ghz is None else round(clock_ghz, 3),
         "copy_lds_gbs": round(cbytes / (cms * 1e-3) / 1e9, 1),
+        "copy_lds_l2_gbs_per_cu": round(lbytes / (lms * 1e-3) / 1e9 / cus, 1),
         "hbm_read_gbs": round(rbytes / (rms * 1e-3) / 1e9, 1),
         "hbm_read_frac_of_peak": round(rbytes / (rms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "probes": (f"MFMA: {wgs} workgroups x 4 waves x {NACC} chains x {mfma_iters} "
                    f"v_mfma_f32_16x16x32_f16 on random fp16; copy: {cbytes >> 20} MiB through LDS "
-                   f"by {cwgs} workgroups; read: {rbytes >> 20} MiB by {rwgs} workgroups"),
+                   f"by {cwgs} workgroups; L2 copy: {cus} workgroups x {l2trips} trips of 64 KiB "
+                   f"cycling through 2 MiB; read: {rbytes >> 20} MiB by {rwgs} workgroups"),
     }
 
 

@@ -102,19 +102,22 @@ __global__ void __launch_bounds__(kThreads) mfma_kernel(const _Float16* frags, i
     *reinterpret_cast<f32x4*>(out + (((int64_t)gw * kNacc + j) * 64 + lane) * 4) = acc[j];
 }
 
-// Workgroup g copies its `share` bytes (in kTrip trips) into a two-stage LDS
-// ring: trip t+1 is in flight while trip t is read back and folded into a
-// running XOR.  Wave w copies 16 KiB of each trip: 1 KiB blocks 16w .. 16w+15.
-__global__ void __launch_bounds__(kThreads) copy_lds_kernel(const char* src, int64_t share,
+// Workgroup g copies `trips` 64 KiB trips into a two-stage LDS ring: trip t
+// is trip (g * first_stride + t) mod ntrips of src.  Trip t+1 is in flight
+// while trip t is read back and folded into a running XOR.  Wave w copies
+// 16 KiB of each trip: 1 KiB blocks 16w .. 16w+15.  With first_stride = trips
+// every workgroup streams its own contiguous share once; with a small src and
+// first_stride = 1 the workgroups cycle through a buffer that stays in L2.
+__global__ void __launch_bounds__(kThreads) copy_lds_kernel(const char* src, int64_t ntrips,
+                                                            int64_t first_stride, int trips,
                                                             uint32_t* out) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * kTrip];
   const int tid = threadIdx.x, wave = tid >> 6;
-  const char* base = src + (int64_t)blockIdx.x * share;
-  const int trips = (int)(share / kTrip);
+  const int64_t first = (int64_t)blockIdx.x * first_stride;
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uint64_t>(&lds[0]);
   auto issue = [&](int t) {
-    // one descriptor per trip keeps every offset below 2^32 whatever the share
-    const u32x4 r = raw_rsrc(base + (int64_t)t * kTrip, (uint32_t)kTrip);
+    // one descriptor per trip keeps every offset below 2^32 whatever the buffer
+    const u32x4 r = raw_rsrc(src + ((first + t) % ntrips) * kTrip, (uint32_t)kTrip);
     const int st = t & 1;
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -209,8 +212,25 @@ int mi_ceiling_copy_lds(const void* src, int64_t bytes, int32_t workgroups, uint
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((workgroups + 255) / 256)), dim3(256), 0, s, out,
                      workgroups);
   if (launched(hip_error)) return 2;
+  const int64_t per_wg = bytes / workgroups / kTrip;
+  if (per_wg > INT32_MAX) return 1;
   hipLaunchKernelGGL(copy_lds_kernel, dim3((unsigned)workgroups), dim3(kThreads), 0, s,
-                     static_cast<const char*>(src), bytes / workgroups, out);
+                     static_cast<const char*>(src), bytes / kTrip, per_wg, (int)per_wg, out);
+  return launched(hip_error);
+}
+
+int mi_ceiling_copy_lds_cycle(const void* src, int64_t bytes, int32_t workgroups, int32_t trips,
+                              uint32_t* out, void* stream, int* hip_error) {
+  if (hip_error) *hip_error = 0;
+  if (!src || !out || workgroups < 1 || trips < 1 || bytes < kTrip || bytes > (int64_t(1) << 40) ||
+      bytes % kTrip != 0 || !aligned16(src))
+    return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((workgroups + 255) / 256)), dim3(256), 0, s, out,
+                     workgroups);
+  if (launched(hip_error)) return 2;
+  hipLaunchKernelGGL(copy_lds_kernel, dim3((unsigned)workgroups), dim3(kThreads), 0, s,
+                     static_cast<const char*>(src), bytes / kTrip, (int64_t)1, (int)trips, out);
   return launched(hip_error);
 }
 

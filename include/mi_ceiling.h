@@ -12,6 +12,9 @@
  *   - mi_ceiling_copy_lds: global -> LDS copies (buffer_load_dwordx4 ... lds,
  *     the GEMM tiles' copy instruction) of a contiguous buffer through a
  *     two-stage LDS ring, nothing else;
+ *   - mi_ceiling_copy_lds_cycle: the same copies, with the workgroups
+ *     cycling through a buffer small enough to stay in L2: the rate at which
+ *     one CU can pull operand rows from L2 into its LDS;
  *   - mi_ceiling_read: 16-byte global loads into registers, nothing else (the
  *     streaming read rate of HBM when the buffer exceeds the 256 MiB MALL).
  * "H100 GEMM L2驻留优化：warp-specialized TMA异步拷贝与RL调优策略"
@@ -33,6 +36,9 @@
  *     of the operands (in the MFMA operand layout).
  *   - copy_lds, read: out[g] is the XOR of every 32-bit word of workgroup g's
  *     contiguous share of src (bytes / workgroups bytes).
+ *   - copy_lds_cycle: with T = bytes / 65536 trips of 64 KiB in src, workgroup
+ *     g copies trips (g + t) mod T for t = 0 .. trips-1, and out[g] is the XOR
+ *     of every 32-bit word of those trips (a trip copied twice cancels).
  *
  * Conventions: pointers are DEVICE pointers, 16-byte aligned, caller-owned;
  * stream is a hipStream_t as void* (NULL: the null stream); each call
@@ -61,6 +67,11 @@ int mi_ceiling_mfma(const void* frags, int32_t workgroups, int32_t iters, float*
  * workgroup copies its share in 64 KiB trips through a two-stage LDS ring. */
 int mi_ceiling_copy_lds(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,
                         void* stream, int* hip_error);
+
+/* bytes a positive multiple of 65536, at most 2^40; trips >= 1 64 KiB trips
+ * per workgroup through the same two-stage LDS ring. */
+int mi_ceiling_copy_lds_cycle(const void* src, int64_t bytes, int32_t workgroups, int32_t trips,
+                              uint32_t* out, void* stream, int* hip_error);
 
 /* bytes a positive multiple of workgroups * 4096, at most 2^40. */
 int mi_ceiling_read(const void* src, int64_t bytes, int32_t workgroups, uint32_t* out,

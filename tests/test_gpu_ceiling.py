@@ -70,6 +70,20 @@ def test_checksum_probes_exact(probe, unit):
     assert np.array_equal(got, want)
 
 
+def test_copy_cycle_probe_exact():
+    ntrips, wgs, trips = 5, 9, 7      # workgroups wrap around the buffer; trips > ntrips
+    rng = np.random.default_rng(8)
+    host = rng.integers(0, 2 ** 32, ntrips * 65536 // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to(DEV)
+    out = ce.copy_lds_cycle(src, wgs, trips)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    per_trip = np.bitwise_xor.reduce(host.reshape(ntrips, -1), axis=1)
+    want = np.array([np.bitwise_xor.reduce(per_trip[[(g + t) % ntrips for t in range(trips)]])
+                     for g in range(wgs)], dtype=np.uint32)
+    assert np.array_equal(got, want)
+
+
 def test_invalid_arguments():
     src = torch.zeros(1024, dtype=torch.int32, device=DEV)
     with pytest.raises(ce.CeilingError):
@@ -87,3 +101,4 @@ def test_measured_ceilings_are_plausible():
     assert m["clock_ghz_under_mfma"] is None or 0.5 < m["clock_ghz_under_mfma"] < 3.0
     assert 1000 < m["hbm_read_gbs"] < 9000
     assert m["copy_lds_gbs"] > 1000
+    assert 5 < m["copy_lds_l2_gbs_per_cu"] < 200
