@@ -29,8 +29,6 @@ sample of the same product on the host cores.
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import math
 import os
@@ -516,6 +514,9 @@ def server_main(args):
             "saturation": server_mode.run(mnk, "closed", requests=max(args.steps, 1) * 200,
                                           depth=8, backend=backend),
         }
+    # the floor of this harness: one empty kernel and its event per request
+    runs["launch"] = {"saturation": server_mode.run(mnk, "closed", requests=max(args.steps, 1) * 200,
+                                                    depth=8, backend="launch")}
     ours, vend = runs["mi_hgemm"], runs["rocblas"]
     sat = ours["saturation"]["achieved_qps"]
     # both at 80% of our sustained rate: latency under a heavy but stable load
@@ -541,7 +542,10 @@ def server_main(args):
                    "parallelism": "none (1 GPU)"},
         "server": runs,
         "context": {"rocblas_sustained_qps": vend["saturation"]["achieved_qps"],
-                    "ours_over_rocblas": round(sat / vend["saturation"]["achieved_qps"], 3)},
+                    "ours_over_rocblas": round(sat / vend["saturation"]["achieved_qps"], 3),
+                    "empty_kernel_sustained_qps": runs["launch"]["saturation"]["achieved_qps"],
+                    "issue_us_mean": {b: runs[b]["saturation"].get("issue_us", {}).get("mean")
+                                      for b in ("mi_hgemm", "rocblas", "launch")}},
         "roofline": None,
         "cpu_baseline": None if args.no_cpu_baseline else server_cpu_baseline(mnk, args.cpu_seconds),
     }

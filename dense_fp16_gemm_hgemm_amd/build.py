@@ -92,7 +92,11 @@ def build(verbose: bool = False) -> str:
     subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
     tmp = OVERLAP_PATH + ".tmp%d" % os.getpid()
-    r = subprocess.run([HIPCC, *COMMON, *DEVICE, "-shared", OVERLAP_SRC, "-o", tmp],
+    # Every inner loop starts on a 64-byte boundary.  The modes' FMA loops are
+    # the same nine instructions; left where the compiler put them, two of the
+    # four straddled three 32-byte fetch blocks instead of two, and ran 1.15-1.22x
+    # slower at high arithmetic intensity for that reason alone.
+    r = subprocess.run([HIPCC, *COMMON, *DEVICE, "-falign-loops=64", "-shared", OVERLAP_SRC, "-o", tmp],
                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         print(r.stdout.decode(errors="replace"), file=sys.stderr)

@@ -19,10 +19,12 @@
 //
 // Backends: the library's own dispatch (mi_hgemm_run), or rocBLAS's
 // rocblas_gemm_ex (fp16 in and out, fp32 compute) on the same operands, for
-// the vendor comparison.
+// the vendor comparison, or "launch": one empty kernel per request, the floor
+// that a HIP launch and its event set for any backend in this harness.  The
+// record also reports the host time each request's issue call took.
 //
 //   mi_hgemm_serve --mnk M_N_K [--mode poisson|closed] [--qps Q] [--requests N]
-//                  [--depth D] [--sets S] [--seed X] [--backend mi_hgemm|rocblas]
+//                  [--depth D] [--sets S] [--seed X] [--backend mi_hgemm|rocblas|launch]
 //                  [--dump DIR]
 // prints one JSON line.  --dump writes set 0's A, B (binary16, row-major, K
 // contiguous) and its C after the run as raw files A.bin, B.bin, C.bin.
@@ -36,6 +38,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <numeric>
 #include <random>
 #include <string>
 #include <thread>
@@ -68,6 +71,8 @@ __device__ inline uint32_t mix32(uint32_t x) {
   x ^= x >> 16;
   return x;
 }
+
+__global__ void empty_kernel() {}
 
 // operand values uniform in (-scale, scale), from a hash of (seed, index)
 __global__ void fill_kernel(_Float16* x, int64_t n, uint32_t seed, float scale) {
@@ -114,7 +119,7 @@ Options parse(int argc, char** argv) {
   }
   if (o.M < 1 || o.N < 1 || o.K < 1 || o.requests < 1 || o.depth < 1 || o.sets < 1 ||
       o.qps <= 0.0 || (o.mode != "poisson" && o.mode != "closed") ||
-      (o.backend != "mi_hgemm" && o.backend != "rocblas"))
+      (o.backend != "mi_hgemm" && o.backend != "rocblas" && o.backend != "launch"))
     die("bad arguments", "see the usage in the source header");
   return o;
 }
@@ -160,7 +165,7 @@ int main(int argc, char** argv) {
     const mi_hgemm_status_t st = mi_hgemm_create(&h, nullptr);
     if (st != MI_HGEMM_OK && st != MI_HGEMM_WARN_TABLE_DEFAULTS)
       die("mi_hgemm_create", mi_hgemm_status_string(st));
-  } else {
+  } else if (o.backend == "rocblas") {
     if (rocblas_create_handle(&rb) != rocblas_status_success) die("rocblas", "create_handle");
     if (rocblas_set_stream(rb, stream) != rocblas_status_success) die("rocblas", "set_stream");
   }
@@ -170,6 +175,9 @@ int main(int argc, char** argv) {
       const mi_hgemm_status_t st = mi_hgemm_run(h, M, N, K, A[s], K, B[s], K, C[s], N,
                                                 MI_HGEMM_LAYOUT_TN, stream);
       if (st != MI_HGEMM_OK) die("mi_hgemm_run", mi_hgemm_status_string(st));
+    } else if (!rb) {
+      hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, stream);
+      check_hip(hipGetLastError(), "empty_kernel");
     } else {
       // row-major C = A Bt^T is column-major C^T (N x M) = Bt (as K x N, transposed) * A^T
       const rocblas_status st = rocblas_gemm_ex(
@@ -189,7 +197,7 @@ int main(int argc, char** argv) {
   std::vector<hipEvent_t> ev(n);
   for (int i = 0; i < n; ++i)
     check_hip(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming), "hipEventCreate");
-  std::vector<double> arrive(n, 0.0), done(n, 0.0);
+  std::vector<double> arrive(n, 0.0), done(n, 0.0), issue_us(n, 0.0);
   std::atomic<int> issued{0}, completed{0};
 
   // completion side: requests finish in order on the one stream
@@ -221,7 +229,9 @@ int main(int argc, char** argv) {
       }
       arrive[i] = now_us();
     }
+    const double ti = now_us();
     issue(i % o.sets);
+    issue_us[i] = now_us() - ti;
     check_hip(hipEventRecord(ev[i], stream), "hipEventRecord");
     issued.store(i + 1, std::memory_order_release);
   }
@@ -250,11 +260,14 @@ int main(int argc, char** argv) {
       "{\"backend\": \"%s\", \"mode\": \"%s\", \"M\": %lld, \"N\": %lld, \"K\": %lld, "
       "\"requests\": %d, \"target_qps\": %s, \"offered_qps\": %.3f, \"achieved_qps\": %.3f, "
       "\"depth\": %d, \"sets\": %d, \"seed\": %llu, \"latency_us\": {\"mean\": %.3f, "
-      "\"p50\": %.3f, \"p90\": %.3f, \"p99\": %.3f, \"max\": %.3f}}\n",
+      "\"p50\": %.3f, \"p90\": %.3f, \"p99\": %.3f, \"max\": %.3f}, "
+      "\"issue_us\": {\"mean\": %.3f, \"p50\": %.3f, \"p99\": %.3f}}\n",
       o.backend.c_str(), o.mode.c_str(), (long long)M, (long long)N, (long long)K, n,
       o.mode == "poisson" ? std::to_string(o.qps).c_str() : "null", offered,
       n / (span * 1e-6), o.depth, o.sets, (unsigned long long)o.seed, sum / n, pct(lat, 0.5),
-      pct(lat, 0.9), pct(lat, 0.99), pct(lat, 1.0));
+      pct(lat, 0.9), pct(lat, 0.99), pct(lat, 1.0),
+      std::accumulate(issue_us.begin(), issue_us.end(), 0.0) / n, pct(issue_us, 0.5),
+      pct(issue_us, 0.99));
 
   for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
   if (h) mi_hgemm_destroy(h);

@@ -52,7 +52,7 @@ def main(argv=None):
     ap.add_argument("--depth", type=int, default=8)
     ap.add_argument("--sets", type=int, default=64)
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--backend", default="mi_hgemm", choices=("mi_hgemm", "rocblas"))
+    ap.add_argument("--backend", default="mi_hgemm", choices=("mi_hgemm", "rocblas", "launch"))
     a = ap.parse_args(argv)
     print(json.dumps(run(a.mnk, a.mode, a.qps, a.requests, a.depth, a.sets, a.seed, a.backend)),
           flush=True)
