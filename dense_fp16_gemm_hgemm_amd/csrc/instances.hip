@@ -90,6 +90,11 @@ namespace mihg {
 #define MIHG_I8_D2TILE3_INSTANCES(X) \
   X(256, 256, 2, 4)
 
+// I8_PP2TILE: X(BM, BN): the ping-pong tile on int8 operands (K tile of 128)
+#define MIHG_I8_PP2TILE_INSTANCES(X) \
+  X(256, 256)                        \
+  X(256, 128)
+
 #define MIHG_I8_KTILE_INSTANCES(X) \
   X(128, 128, 2, 4, 256, 2)        \
   X(128, 128, 2, 2, 256, 2)        \
@@ -208,6 +213,7 @@ namespace mihg {
 #define INSTANTIATE_I8_D2TILE3(BM, BN, WGM, WGN) \
   template __global__ void i8_d2tile3_kernel<BM, BN, WGM, WGN>(GemmArgs);
 #define INSTANTIATE_PPTILE(BM, BN) template __global__ void pptile_kernel<BM, BN>(GemmArgs);
+#define INSTANTIATE_I8_PP2TILE(BM, BN) template __global__ void i8_pp2tile_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_PP2TILE(BM, BN) template __global__ void pp2tile_kernel<BM, BN, 16>(GemmArgs);
 #define INSTANTIATE_PP2TILESC(BM, BN) template __global__ void pp2tilesc_kernel<BM, BN>(GemmArgs);
 #define INSTANTIATE_PP2TILESK(BM, BN) template __global__ void pp2tilesc_kernel<BM, BN, true>(GemmArgs);
@@ -261,6 +267,7 @@ MIHG_SKINNY_INSTANCES(INSTANTIATE_SKINNY)
 template __global__ void i8_generic_kernel<64, 64, 2, 2, 16>(GemmArgs);
 MIHG_I8_D2TILE_INSTANCES(INSTANTIATE_I8_D2TILE)
 MIHG_I8_D2TILE3_INSTANCES(INSTANTIATE_I8_D2TILE3)
+MIHG_I8_PP2TILE_INSTANCES(INSTANTIATE_I8_PP2TILE)
 MIHG_I8_KTILE_INSTANCES(INSTANTIATE_I8_KTILE)
 MIHG_I8_KTILE_B_INSTANCES(INSTANTIATE_I8_KTILE_B)
 MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
@@ -286,6 +293,10 @@ MIHG_I8_KTILE_NT_INSTANCES(INSTANTIATE_I8_KTILE_NT)
   {"i8_d2tile3_" #BM "x" #BN "_w" #WGM "x" #WGN "_m16", FAMILY_TILE, BM, BN, 128, WGM * WGN,   \
    16, 1, 1, (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_i8_d2tile3<BM, BN, WGM, WGN>,          \
    &grid_tile<BM, BN>, DTYPE_I8},
+#define I8_PP2TILE_DESC(BM, BN)                                                            \
+  {"i8_pp2tile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 128, 8, 16, 1, 1,                \
+   (3 * BM + 2 * BN) * kD2Row * 2, 0, &launch_i8_pp2tile<BM, BN>, &grid_tile<BM, BN>,         \
+   DTYPE_I8},
 #define PPTILE_DESC(BM, BN)                                                                \
   {"pptile_" #BM "x" #BN "_w8_m16", FAMILY_TILE, BM, BN, 64, 8, 16, 1, 1,                     \
    2 * (BM + BN) * kD2Row * 2, 0, &launch_pptile<BM, BN>, &grid_tile<BM, BN>},
@@ -381,6 +392,7 @@ const KernelDesc kKernels[] = {
      &launch_i8_generic<64, 64, 2, 2, 16>, &grid_tile<64, 64>, DTYPE_I8},
     MIHG_I8_D2TILE_INSTANCES(I8_D2TILE_DESC)
     MIHG_I8_D2TILE3_INSTANCES(I8_D2TILE3_DESC)
+    MIHG_I8_PP2TILE_INSTANCES(I8_PP2TILE_DESC)
     MIHG_I8_KTILE_INSTANCES(I8_KTILE_DESC)
     MIHG_I8_KTILE_B_INSTANCES(I8_KTILE_B_DESC)
     MIHG_I8_KTILE_NT_INSTANCES(I8_KTILE_NT_DESC)

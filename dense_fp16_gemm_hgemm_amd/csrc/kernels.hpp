@@ -1538,11 +1538,15 @@ pptile_kernel(GemmArgs p) {
 // before the barrier that opens its first reads (phase 2kt+1).
 // SK: the instance splits K (GemmArgs::splitk slices, the shared fix-up);
 // without it the slice bookkeeping compiles away.
-template <int BM, int BN, bool SC, int MF = 16, bool SK = false>
+// Op: the element types (OpF16, OpI8); a K tile is one 128-byte LDS row of
+// each operand row (64 binary16 or 128 int8 elements).
+template <typename Op, int BM, int BN, bool SC, int MF = 16, bool SK = false>
 __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
-  using MM = Mfma<MF>;
-  constexpr int BK = 64, KSTEPS = BK / MM::KI, CPS = MM::KI / 8;  // CPS: 16-byte chunks per k-step
-  static_assert(!SC || MF == 16, "the staged C store takes 16 x 16 blocks");
+  using MM = typename Op::template Mma<MF>;
+  constexpr int EB = Op::kEB, CB = Op::kCB;
+  constexpr int BK = 128 / EB, EPC = 16 / EB;            // K elements per tile and per 16-byte chunk
+  constexpr int KSTEPS = BK / MM::KI, CPS = MM::KI / EPC;  // CPS: 16-byte chunks per k-step
+  static_assert(!SC || (MF == 16 && CB == 2), "the staged C store takes 16 x 16 binary16 blocks");
   constexpr int WTM = BM / 2, WTN = BN / 4;
   constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr int A_BLK = BM / 8 / 4, B_BLK = BN / 8 / 4;  // 1 KiB copies per wave of the copying group
@@ -1577,36 +1581,36 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
   // start at the slice's first k and end where the full rows end.
   const int drow = lane >> 3;
   const int dch0 = (lane & 7) ^ (lane >> 4), dch1 = dch0 ^ 4;
-  const u32x4 rda = raw_rsrc(static_cast<const _Float16*>(p.A) + m0 * lda + k_begin,
-                             (uint32_t)((min(BM, M - m0) * lda - k_begin) * 2));
-  const u32x4 rdb = raw_rsrc(static_cast<const _Float16*>(p.B) + n0 * ldb + k_begin,
-                             (uint32_t)((min(BN, N - n0) * ldb - k_begin) * 2));
+  const u32x4 rda = raw_rsrc(static_cast<const char*>(p.A) + (m0 * lda + k_begin) * EB,
+                             (uint32_t)((min(BM, M - m0) * lda - k_begin) * EB));
+  const u32x4 rdb = raw_rsrc(static_cast<const char*>(p.B) + (n0 * ldb + k_begin) * EB,
+                             (uint32_t)((min(BN, N - n0) * ldb - k_begin) * EB));
   const int64_t ldx = grp == 1 ? lda : ldb;
-  const uint32_t v0 = (uint32_t)(drow * ldx * 2 + dch0 * 16), v1 = (uint32_t)(drow * ldx * 2 + dch1 * 16);
-  const bool mask_k = (KS & 63) != 0;
+  const uint32_t v0 = (uint32_t)(drow * ldx * EB + dch0 * 16), v1 = (uint32_t)(drow * ldx * EB + dch1 * 16);
+  const bool mask_k = (KS % BK) != 0;
   const uint32_t lds0 = lds_addr(lds);
   // this wave's copies of K tile t: group 1 copies its quarter of A's rows into
   // A stage `st` (copy_a), group 0 its quarter of B's rows into B stage `st`
   // (copy_b); chunks at or past K read 0
   auto copy_a = [&](int st, int t) {
-    const uint32_t kb = (uint32_t)(t * BK) * 2;
+    const uint32_t kb = (uint32_t)(t * BK) * EB;
 #pragma unroll
     for (int x = 0; x < A_BLK; ++x) {
       const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (t * BK + ch * 8 < KS);
+      const bool kin = !mask_k || (t * BK + ch * EPC < KS);
       const int blk = w4 * A_BLK + x;
-      dma16(rda, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * lda * 2) + kb,
+      dma16(rda, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * lda * EB) + kb,
             lds0 + (uint32_t)((st * A_STRIDE + blk * 8 * kD2Row) * 2));
     }
   };
   auto copy_b = [&](int st, int t) {
-    const uint32_t kb = (uint32_t)(t * BK) * 2;
+    const uint32_t kb = (uint32_t)(t * BK) * EB;
 #pragma unroll
     for (int x = 0; x < B_BLK; ++x) {
       const int ch = (x & 1) ? dch1 : dch0;
-      const bool kin = !mask_k || (t * BK + ch * 8 < KS);
+      const bool kin = !mask_k || (t * BK + ch * EPC < KS);
       const int blk = w4 * B_BLK + x;
-      dma16(rdb, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * ldb * 2) + kb,
+      dma16(rdb, kin ? ((x & 1) ? v1 : v0) : kOOB, (uint32_t)(blk * 8 * ldb * EB) + kb,
             lds0 + (uint32_t)((B_OFF + st * B_STRIDE + blk * 8 * kD2Row) * 2));
     }
   };
@@ -1717,8 +1721,8 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
       return;
   }
 
-  char* Cw = static_cast<char*>(p.C) + m0 * ldc * 2;
-  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
+  char* Cw = static_cast<char*>(p.C) + m0 * ldc * CB;
+  const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * CB));
   bool staged = false;
   if constexpr (SC) {
     constexpr int SCR_HALVES = 16 * WTN;
@@ -1742,10 +1746,10 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
 #pragma unroll
         for (int g = 0; g < MM::NACC / 4; ++g) {
           const int j = n0 + w4 * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
-          f32x4 v;
+          typename Op::acc4_t v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[fm][fn][4 * g + e];
-          OpF16::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * 2) : kOOB, v);
+          Op::store4(rsc, j < N ? (uint32_t)((i * ldc + j) * CB) : kOOB, v);
         }
     }
   } else {
@@ -1759,19 +1763,23 @@ __device__ __forceinline__ void pp2_body(const GemmArgs& p) {
           const int j = n0 + w4 * WTN + fn * MF + g * (256 / MF) + 4 * (lane / MF);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            OpF16::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * 2) : kOOB,
-                          acc[fm][fn][4 * g + e]);
+            Op::store1(rsc, j + e < N ? (uint32_t)((i * ldc + j + e) * CB) : kOOB,
+                       acc[fm][fn][4 * g + e]);
         }
     }
   }
 }
 template <int BM, int BN, int MF, bool SK = false>
 __global__ void __launch_bounds__(512) pp2tile_kernel(GemmArgs p) {
-  pp2_body<BM, BN, false, MF, SK>(p);
+  pp2_body<OpF16, BM, BN, false, MF, SK>(p);
 }
 template <int BM, int BN, bool SK = false>
 __global__ void __launch_bounds__(512) pp2tilesc_kernel(GemmArgs p) {
-  pp2_body<BM, BN, true, 16, SK>(p);
+  pp2_body<OpF16, BM, BN, true, 16, SK>(p);
+}
+template <int BM, int BN>
+__global__ void __launch_bounds__(512) i8_pp2tile_kernel(GemmArgs p) {
+  pp2_body<OpI8, BM, BN, false, 16, false>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -2399,6 +2407,12 @@ template <int BM, int BN, int MF, bool SK = false>
 hipError_t launch_pp2tile(const GemmArgs& a, hipStream_t s) {
   const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * (SK ? a.splitk : 1);
   hipLaunchKernelGGL((pp2tile_kernel<BM, BN, MF, SK>), dim3((unsigned)g), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+template <int BM, int BN>
+hipError_t launch_i8_pp2tile(const GemmArgs& a, hipStream_t s) {
+  const int64_t g = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((i8_pp2tile_kernel<BM, BN>), dim3((unsigned)g), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 template <int BM, int BN, bool SK = false>

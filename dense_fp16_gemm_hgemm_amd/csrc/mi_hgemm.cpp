@@ -322,10 +322,11 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
                                  : (M <= 32 ? "ktile_32x64_w2x2_k128_s3_nt" : "ktile_32x64_w2x2_k128_s3b3_sc"));
   const int k16 = find_kernel(i8 ? "i8_ktile_16x64_w1x4_k256_s3_nt" : "ktile_16x64_w1x4_k128_s3_nt");
   const int k128d = find_kernel(i8 ? "i8_d2tile_128x128_w2x2_m16" : "d2tile_128x128_w2x2_m16_sc");
-  // binary16 with five eighths of a wave of 256x256 tiles or more: the
-  // ping-pong tile (two wave groups taking turns at the matrix pipes) measured
-  // 4-14% ahead of d2tile3 from 172 tiles up (1024x11008x4096 .. 8192^3)
-  const int kpp = i8 ? -1 : find_kernel("pp2tile_256x256_w8_m16_sc");
+  // five eighths of a wave of 256x256 tiles or more: the ping-pong tile (two
+  // wave groups taking turns at the matrix pipes) measured 4-14% ahead of
+  // d2tile3 from 172 tiles up (1024x11008x4096 .. 8192^3) in binary16, 5-9%
+  // in int8
+  const int kpp = find_kernel(i8 ? "i8_pp2tile_256x256_w8_m16" : "pp2tile_256x256_w8_m16_sc");
   // binary16 with 96 to 159 tiles of 256x128 over a K of 8192 or more and an
   // N of 2048 or more: the ping-pong 256x128 tile, K split in two
   // (1024x4096x11008 cold: 99.8 against 108.2 us for the deep-K 128x128

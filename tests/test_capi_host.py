@@ -324,7 +324,8 @@ def test_int8_alignment_class_and_heuristic(inspect_handle):
     for M, N, K in ((8192, 8192, 8192), (1024, 4096, 4096), (64, 4096, 11008), (16, 4096, 4096)):
         n, _ = choice(M, N, K)
         assert n.startswith("i8_") and n != names[generic], (M, N, K, n)
-    assert choice(8192, 8192, 8192)[0] == "i8_d2tile3_256x256_w2x4_m16"
+    assert choice(8192, 8192, 8192)[0] == "i8_pp2tile_256x256_w8_m16"
+    assert choice(1024, 11008, 4096)[0] == "i8_pp2tile_256x256_w8_m16"
     assert choice(1024, 4096, 4096)[0] == "i8_ktile_128x128_w2x4_k256_s3b2"
     assert choice(16, 4096, 4096)[0] == "i8_ktile_16x64_w1x4_k256_s3_nt"
     # the 16-byte class in int8 elements: K, lda, ldb multiples of 16, ldc of 4

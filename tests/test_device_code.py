@@ -106,6 +106,10 @@ def mangled_i8(name):
         kind, bm, bn, wm, wn = m.groups()
         return (f"_ZN4mihg{len(kind) + 10}i8_{kind}_kernelILi{bm}ELi{bn}ELi{wm}ELi{wn}"
                 "EEEvNS_8GemmArgsE")
+    m = re.fullmatch(r"pp2tile_(\d+)x(\d+)_w8_m16", name)
+    if m:
+        bm, bn = m.groups()
+        return f"_ZN4mihg17i8_pp2tile_kernelILi{bm}ELi{bn}EEEvNS_8GemmArgsE"
     m = re.fullmatch(r"ktile_(\d+)x(\d+)_w(\d+)x(\d+)_k(\d+)_s(\d+)(?:b(\d+))?", name)
     if m:
         bm, bn, wm, wn, bk, s, sb = m.groups()
