@@ -981,13 +981,20 @@ extern "C" mi_hgemm_status_t mi_hgemm_tune(mi_hgemm_handle_t h, int64_t M, int64
     // up to two workgroups per CU: a split can also pay where the tiles just
     // fill the CUs once (two small-LDS workgroups share a CU's copy bandwidth)
     if (!kd.splitk_ok || !h->ws || tiles >= 512) return;
+    // the slices of a tile are adjacent workgroups, so the XCD remap (which
+    // assumes one tile per workgroup) stays off; the raster height still
+    // decides which tiles share an XCD's L2
     for (int s = 2; s <= 16; s *= 2) {
       int64_t chunk = K;
       if (K / s < 256 || tiles * s > 1024 || effective_split(kd, M, N, K, s, &chunk) < s) break;
-      Config c;
-      c.kernel = k;
-      c.splitk = s;
-      cands.push_back(c);
+      for (int g : {1, 4, 8}) {
+        if (heuristic_only && g != 1) continue;
+        Config c;
+        c.kernel = k;
+        c.splitk = s;
+        c.group_m = g;
+        cands.push_back(c);
+      }
     }
   };
   for (int k = 0; k < kNumKernels; ++k) {
