@@ -1516,8 +1516,9 @@ pptile_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Full-tile ping-pong family ("pp2tile"): BM x BN x 64 tiles, 8 waves in two
-// groups of four; every SIMD holds one wave of each group.  Time is cut into
+// Full-tile ping-pong family ("pp2tile"): BM x BN tiles whose K tiles are one
+// 128-byte row deep (64 binary16 or 128 int8 values), 8 waves in two groups
+// of four; every SIMD holds one wave of each group.  Time is cut into
 // phases by workgroup barriers.  In each phase one group multiplies a whole K
 // tile -- all 2 x FM x FN MFMAs back to back from fragments already in its
 // registers, at raised wave priority -- while the other group reads its
