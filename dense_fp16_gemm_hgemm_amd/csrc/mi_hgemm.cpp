@@ -326,6 +326,12 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   // wave groups taking turns at the matrix pipes) measured 4-14% ahead of
   // d2tile3 from 172 tiles up (1024x11008x4096 .. 8192^3) in binary16, 5-9%
   // in int8
+  // Its raster: up to one wave of tiles (256 or fewer) the XCD-local groups of
+  // 8 tile rows (g8 x1) measured 0-20% ahead of row-major order over
+  // 4096x4096, 8192x2048 and 2048x8192 at K = 128..2048 (e.g. 8192x2048x1024:
+  // 32.7 against 37.7 us); from four waves up row-major order (g1 x0) was
+  // 2-26% ahead on 8192x8192 at K = 64..2048 (e.g. 8192x8192x256: 52.8
+  // against 60.6 us), and at two waves the two were within 3% at K >= 256.
   const int kpp = find_kernel(i8 ? "i8_pp2tile_256x256_w8_m16" : "pp2tile_256x256_w8_m16_sc");
   // binary16 with 96 to 159 tiles of 256x128 over a K of 8192 or more and an
   // N of 2048 or more: the ping-pong 256x128 tile, K split in two
@@ -335,7 +341,10 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   const int kppsk = i8 ? -1 : find_kernel("pp2tile_256x128_w8_m16_sc_sk");
   int64_t chunk2 = K;
   if (M > 64 && kpp >= 0 && tiles(kpp) >= 160) {
-    pick(kpp, 1, 0, 1);
+    if (tiles(kpp) <= 256)
+      pick(kpp, 8, 1, 1);
+    else
+      pick(kpp, 1, 0, 1);
   } else if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
     pick(k256, 8, 1, 1);
   } else if (M > 64 && N >= 2048 && kppsk >= 0 && K >= 8192 && tiles(kppsk) >= 96 && tiles(kppsk) < 160 &&

@@ -154,6 +154,11 @@ def test_heuristic_picks_by_shape(inspect_handle):
     assert choice(4096, 4096, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
     assert choice(1024, 14336, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
     assert choice(1024, 11008, 4096) == ("pp2tile_256x256_w8_m16_sc", 1)
+    # its raster: XCD-local groups of 8 tile rows up to one wave, row-major above
+    assert plan(h, 4096, 4096, 1024)[2:4] == (8, 1)
+    assert plan(h, 1024, 14336, 4096)[2:4] == (8, 1)
+    assert plan(h, 8192, 4096, 1024)[2:4] == (1, 0)
+    assert plan(h, 8192, 8192, 8192)[2:4] == (1, 0)
     # 96..159 tiles of 256x128 over a long K: the same tile split in two along K
     assert choice(1024, 4096, 11008) == ("pp2tile_256x128_w8_m16_sc_sk", 2)
     assert choice(8192, 512, 8192)[0] != "pp2tile_256x128_w8_m16_sc_sk"   # narrow N
