@@ -386,8 +386,13 @@ Config select_uncached(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t
   // nearest tuned shape in log2(M, N, K), within a factor of two overall
   double best = 1.0 + 1e-9;
   const Config* pick = nullptr;
+  // (within a factor of two overall means within a factor of two in each of
+  // M, N and K: integer tests skip the logarithms for every other entry)
+  auto near = [](int64_t x, int64_t t) { return t <= 2 * x && x <= 2 * t; };
   for (const auto& kv : h->table) {
-    if (kv.first.cls != key.cls) continue;
+    if (kv.first.cls != key.cls || !near(M, kv.first.M) || !near(N, kv.first.N) ||
+        !near(K, kv.first.K))
+      continue;
     const double d = std::fabs(std::log2((double)M / kv.first.M)) +
                      std::fabs(std::log2((double)N / kv.first.N)) +
                      std::fabs(std::log2((double)K / kv.first.K));
