@@ -487,6 +487,19 @@ def test_shape_sweep_sample(lib, p):
     check_tolerance(got, oracle.hgemm_tn(A, Bt), p.name)
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 3000, 520), (100, 7000, 4104), (5000, 304, 3000),
+                                   (70, 9000, 1504), (600, 600, 6000), (3000, 3000, 200),
+                                   (3000, 200, 3000), (48, 11000, 700)])
+def test_off_grid_shapes_through_dispatch(lib, M, N, K):
+    """Shapes between the tuned grid's points run the nearest tuned shape's
+    configuration (or the built-in rules when none is within a factor of two):
+    every element within tolerance, with ragged tails in M, N and K."""
+    A, Bt = rand_problem(M, N, K, "randn", seed=M + 3 * N + 7 * K)
+    dA, dB = gpu(A), gpu(Bt)
+    log(f"off-grid {M}x{N}x{K}: {lib.plan(dA, dB)}")
+    check_tolerance(host(lib.run(dA, dB)), oracle.hgemm_tn(A, Bt), f"off-grid {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N", [(128, 256), (64, 64)])
 def test_long_k_integer_bitexact(lib, M, N):
     """K = 65536: every partial sum of small integers is exact in fp32 (|sum| <

@@ -68,3 +68,44 @@ def test_evidence_of_a_run_keeps_the_sections_it_did_not_retune(tmp_path):
     make_table.write_evidence(str(fresh), ev, "gpu")
     assert [ln for ln in fresh.read_text(encoding="utf-8").splitlines()
             if ln.startswith("## ")] == ["## 64x64x64", "## 128x64x64"]
+
+
+def test_off_grid_shapes_take_the_nearest_grid_entry(tmp_path):
+    """Between grid points the dispatcher serves a shape with the tuned entry
+    nearest in log2(M) + log2(N) + log2(K) if that sum is at most 1, else with
+    the built-in rules; checked against that rule worked out here over the
+    shipped table's binary16 rows.  The shapes have one nearest entry (no tie)
+    and N and K multiples of 8, so that the operands are in the 16-byte class."""
+    import math
+
+    rows = [r for r in table_rows() if r[5] == "a16"]
+    entries = {(int(r[1]), int(r[2]), int(r[3])): (r[6], int(r[7]), int(r[8])) for r in rows}
+    st, h = mh.mi_hgemm_create_ex(TABLE, mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_OK
+    st, rules = mh.mi_hgemm_create_ex(str(tmp_path / "absent.tsv"), mh.MI_HGEMM_CREATE_NO_DEVICE)
+    assert st == mh.MI_HGEMM_WARN_TABLE_DEFAULTS
+    names = mh.kernel_names()
+    base = 0x7F0000000000
+
+    def plan(handle, M, N, K):
+        r = mh.mi_hgemm_plan(handle, M, N, K, base, K, base + (1 << 36), K, base + (2 << 36), N)
+        assert r[0] == mh.MI_HGEMM_OK
+        return names[r[1]], r[2], r[3]
+
+    near = far = 0
+    try:
+        for M, N, K in [(1000, 3000, 520), (100, 7000, 4104), (5000, 304, 3000), (70, 9000, 1504),
+                        (600, 600, 6000), (3000, 3000, 200), (3000, 200, 3000), (48, 11000, 700)]:
+            dist = sorted((sum(abs(math.log2(a / b)) for a, b in zip((M, N, K), key)), key)
+                          for key in entries)
+            assert dist[1][0] - dist[0][0] > 1e-6, (M, N, K, dist[:2])
+            if dist[0][0] <= 1:
+                assert plan(h, M, N, K) == entries[dist[0][1]], (M, N, K, dist[0][1])
+                near += 1
+            else:
+                assert plan(h, M, N, K) == plan(rules, M, N, K), (M, N, K)
+                far += 1
+        assert near >= 5 and far >= 2
+    finally:
+        mh.mi_hgemm_destroy(h)
+        mh.mi_hgemm_destroy(rules)
