@@ -19,7 +19,7 @@
  *   - same page, 集成步骤 / correctness paragraph: results are judged by
  *     relative error against a library GEMM, so the oracle is the exact
  *     definition, rounded once.
- * Readings where the pages are silent (each listed in the design doc):
+ * Readings where the pages are silent:
  *   - the sum is taken in binary64 in index order k = 0..K-1, one result per
  *     (i, j); every product of two binary16 values is exact in binary64
  *     (11-bit x 11-bit significands), so the only roundings are the K-1
