@@ -1,6 +1,6 @@
 // Compiled kernel instances of the TN half-precision GEMM and their registry.
 //
-// The instance set spans the tuner's search space (a9): workgroup tiles from
+// The instance set spans the tuner's search space: workgroup tiles from
 // 16 to 256 in M and N, 4 or 8 waves, both gfx950 fp16 MFMA shapes, and the
 // skinny direct-to-register family for small M.  Tile sizes start from the
 // menus of "H100 GEMM L2驻留优化：warp-specialized TMA异步拷贝与RL调优策略"

@@ -74,7 +74,7 @@ __device__ inline h8 zero_h8() {
   return z;
 }
 
-// Workgroup id -> output tile (a2).  [P1] 正文 paragraph 2 and [P2] 正文
+// Workgroup id -> output tile.  [P1] 正文 paragraph 2 and [P2] 正文
 // paragraph 3 put the lever in keeping operand panels cache-resident; on
 // MI355X each of the 8 XCDs has its own L2 and consecutive workgroup ids are
 // dispatched round-robin over the XCDs.  With xcd_remap the id is first
@@ -99,7 +99,7 @@ __device__ inline void tile_coords(int pid, int tiles_m, int tiles_n, int group_
 }
 
 // LDS tile rows hold 64 halves = 8 chunks of 16 bytes.  The chunk index is
-// XORed with a function of the row (a3/a5): 16 consecutive rows read at one
+// XORed with a function of the row: 16 consecutive rows read at one
 // logical chunk then touch 16 distinct (row parity, chunk) pairs and 8
 // consecutive rows 8 distinct chunks, so ds_read_b128 of an MFMA fragment and
 // ds_write_b128 of a loaded row are free of bank conflicts whether the LDS
@@ -109,7 +109,7 @@ __device__ inline void tile_coords(int pid, int tiles_m, int tiles_n, int group_
 // of a 128-byte row).
 __device__ inline int swz(int row, int chunk) { return chunk ^ ((row ^ (row >> 3)) & 7); }
 
-// Buffer resources (a8).  A raw buffer descriptor bounds every access by its
+// Buffer resources.  A raw buffer descriptor bounds every access by its
 // record count: loads past the end return 0 and stores past the end are
 // dropped.  Each workgroup builds descriptors whose range ends at the last
 // valid row of its tile, so rows beyond M or N need no code at all, and a
@@ -203,7 +203,7 @@ struct OpI8 {
 // Tile family: BM x BN x 64 workgroup tiles, WGM x WGN waves, 2 LDS stages,
 // operands in the 16-byte alignment class.
 //
-// LDS rows are padded from 128 to 144 bytes (a3/a5).  A 16-byte read of row r
+// LDS rows are padded from 128 to 144 bytes.  A 16-byte read of row r
 // then starts at 4-byte bank 36*r mod 64: 16 consecutive rows read at one
 // chunk start at 16 distinct multiples of 4, and 8 consecutive rows at 8
 // distinct multiples of 4 mod 32, so the MFMA fragment reads (16 or 32 rows at
@@ -214,11 +214,11 @@ struct OpI8 {
 //
 // Per K tile (one trip of the loop, a single basic block):
 //   * 16-byte buffer loads of tile k+1 into registers are issued first, so
-//     they are in flight during tile k's MFMAs (a4).  The row of each load
+//     they are in flight during tile k's MFMAs.  The row of each load
 //     slot and the K position are scalar offsets, so the loads cost no VALU;
 //   * tile k's fragments are read from LDS one MFMA step ahead of use
-//     (register double buffer), and the MFMAs run (a5, a6);
-//   * tile k+1 is written to the other LDS stage (a3) and one barrier ends the
+//     (register double buffer), and the MFMAs run;
+//   * tile k+1 is written to the other LDS stage and one barrier ends the
 //     trip; the next tile's first fragments are read right after it, while
 //     the last MFMAs are still in the pipe.
 // The last trip loads a tile past K, which the descriptors turn into zeros.
@@ -377,7 +377,7 @@ tile_kernel(GemmArgs p) {
   else
     tile_main_loop<BM, BN, WGM, WGN, MF, true>(p, lds, rsa, rsb, acc);
 
-  // Epilogue (a7): fp32 -> fp16 round-to-nearest-even, alpha = 1, beta = 0;
+  // Epilogue: fp32 -> fp16 round-to-nearest-even, alpha = 1, beta = 0;
   // 8-byte stores along N, rows beyond M dropped by the descriptor.
   _Float16* Cw = static_cast<_Float16*>(p.C) + m0 * ldc;
   const auto rsc = make_rsrc(Cw, (uint32_t)(min(BM, M - m0) * ldc * 2));
@@ -2083,7 +2083,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) i8_ktile_nt_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------
-// Element-wise instance: any alignment, any leading dimensions (a8).  Same
+// Element-wise instance: any alignment, any leading dimensions.  Same
 // tiling and arithmetic as the tile family, but every global access is a
 // 2-byte access with its own bounds check; it exists for operands outside the
 // 16-byte class and as the tuner's reference.

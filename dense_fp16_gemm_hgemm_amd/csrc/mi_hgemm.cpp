@@ -9,11 +9,11 @@
 //   * argument validation and status codes (the alignment rules of [P3] §3.1
 //     and §6.1: misaligned vector copies are undefined, so alignment is decided
 //     on the host and misaligned operands take the element-wise instance);
-//   * dispatch (a1): (M, N, K, alignment class) -> table entry, else the nearest
+//   * dispatch: (M, N, K, alignment class) -> table entry, else the nearest
 //     tuned shape, else built-in heuristics -> one launch on the caller's
 //     stream, with nothing rebuilt or allocated per call ([P3] §8 lists
 //     per-launch rebuilding as a classic mistake);
-//   * the shape -> config table file and the tuner (a9), which replaces the
+//   * the shape -> config table file and the tuner, which replaces the
 //     pages' RL agent ([P1] 正文 paragraph 4, [P2] 正文 paragraph 2) with an
 //     exhaustive or pruned timed sweep over the compiled instances and raster
 //     settings, checked for correctness before it may win.
@@ -405,7 +405,7 @@ Config select_uncached(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t
   return heuristic(M, N, K, cls);
 }
 
-// Dispatch (a1): the exact table entry, else the nearest tuned shape, else the
+// Dispatch: the exact table entry, else the nearest tuned shape, else the
 // heuristic -- resolved once per (M, N, K, class) and then looked up.
 // remember = false resolves a miss without storing it (no host allocation).
 Config select(mi_hgemm_ctx* h, int64_t M, int64_t N, int64_t K, int32_t cls,

@@ -1,4 +1,4 @@
-// Stage arithmetic of the LDS rings of the direct-to-LDS tile kernels (a4):
+// Stage arithmetic of the LDS rings of the direct-to-LDS tile kernels:
 // which stage a trip reads, which stages its copies write, which K tiles
 // those copies carry, the order they are issued in, and how many copies a
 // wave may leave in flight at a trip's end.  The kernels take every one of
