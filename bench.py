@@ -555,7 +555,7 @@ def server_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
     if args.server:
