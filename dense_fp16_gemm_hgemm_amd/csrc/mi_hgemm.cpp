@@ -275,10 +275,10 @@ int64_t effective_split(const KernelDesc& kd, int64_t M, int64_t N, int64_t K, i
 // timing every instance over the LLM projection and square shapes on MI355X:
 //  - the binary16 picks stage C through LDS ("_sc"): whole row-segment stores
 //    make short-K shapes up to 1.2-1.3x faster and cost nothing at long K;
-//  - one partial wave of 256x256 tiles beats more waves of smaller tiles down
-//    to three quarters of a wave (the chip is power-bound: idle CUs buy clock
-//    for the busy ones); for binary16 the ping-pong 256x256 tile (pp2tile)
-//    does so down to five eighths of a wave;
+//  - one partial wave of 256x256 tiles beats more waves of smaller tiles (the
+//    chip is power-bound: idle CUs buy clock for the busy ones); in its
+//    ping-pong form (pp2tile, binary16 and int8) down to five eighths of a
+//    wave;
 //  - below that, two or more full waves of 128x128 direct-to-LDS tiles win, at
 //    every K (14-33% ahead of a half wave of 256x256 tiles on the shape sweep);
 //  - below that, the deep-K tiles (K step 128) win: 128x128, then 64x64, then
@@ -309,7 +309,6 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
   };
   // the int8 instances with the same tiles and a K step of the same bytes
   const bool i8 = dtype == mihg::DTYPE_I8;
-  const int k256 = find_kernel(i8 ? "i8_d2tile3_256x256_w2x4_m16" : "d2tile3_256x256_w2x4_m16_sc");
   const int k128 = find_kernel(i8 ? "i8_ktile_128x128_w2x4_k256_s3b2" : "ktile_128x128_w2x4_k128_s3b2_sc");
   // When the output is one row of tiles B is streamed through once: those
   // tiles copy it with the non-temporal policy ("_nt"), which
@@ -345,8 +344,6 @@ Config heuristic(int64_t M, int64_t N, int64_t K, int32_t cls) {
       pick(kpp, 8, 1, 1);
     else
       pick(kpp, 1, 0, 1);
-  } else if (M > 64 && k256 >= 0 && tiles(k256) >= 192) {
-    pick(k256, 8, 1, 1);
   } else if (M > 64 && N >= 2048 && kppsk >= 0 && K >= 8192 && tiles(kppsk) >= 96 && tiles(kppsk) < 160 &&
              effective_split(kKernels[kppsk], M, N, K, 2, &chunk2) == 2) {
     pick(kppsk, 1, 0, 2);
