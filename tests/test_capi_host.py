@@ -199,7 +199,7 @@ def test_nearest_table_entry_drops_a_split_that_does_not_fit(tmp_path, monkeypat
         names = mh.kernel_names()
         r = plan(h, 8192, 14336, 4096)
         assert names[r[1]] == "dtile_256x128_w2x2_m16_s4" and r[4] == 1
-        r = plan(h, 8192, 14336, 6144)                # nearest entry, same verdict
+        r = plan(h, 8192, 14336, 6144)                # nearest entry, same result
         assert names[r[1]] == "dtile_256x128_w2x2_m16_s4" and r[4] == 1
     finally:
         mh.mi_hgemm_destroy(h)
